@@ -1,0 +1,74 @@
+"""Plant plausible slips in a private copy of the oracle and check that a pin catches each.
+
+The mutation happens on the CPU, in a temporary copy of the oracle package; the real
+oracle is never modified.  A mutant that every pin lets through marks a hole in the pins.
+"""
+
+import importlib
+import os
+import shutil
+import sys
+
+import pytest
+
+import pins
+
+ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
+
+# (file, original text, planted slip, what the slip means)
+MUTANTS = [
+    ("router.py", "q = s + b[None, :]", "q = sigmoid_scores(z + b[None, :])", "bias inside the sigmoid"),
+    ("router.py", "gates[lo:hi] = gate_values(s, i, normalize)", "gates[lo:hi] = gate_values(q, i, normalize)",
+     "gates from s + b"),
+    ("router.py", 'order = np.argsort(-q, axis=1, kind="stable")', 'order = np.argsort(q, axis=1, kind="stable")[:, ::-1]',
+     "ties to the higher index"),
+    ("router.py", "return widen(x) @ widen(w).T", "return widen(x)[:, :-1] @ widen(w)[:, :-1].T", "dropped last term"),
+    ("router.py", "1.0 / (1.0 + np.exp(-z))", "1.0 / (1.0 + np.exp(z))", "sigmoid sign"),
+    ("router.py", "gap = q[rows, order[:, k - 1]] - q[rows, order[:, k]]",
+     "gap = q[rows, order[:, 0]] - q[rows, order[:, k]]", "gap from the first choice"),
+    ("router.py", "return sel / sel.sum(axis=1, keepdims=True)", "return sel / s.sum(axis=1, keepdims=True)",
+     "normalised over every expert"),
+    ("router.py", "z = widen(x[lo:hi]) @ w64.T", "z = widen(x[lo:hi]) @ w64[::-1].T", "expert rows reversed"),
+    ("balance.py", "db = db_raw - db_raw.mean()", "db = db_raw", "no re-centre"),
+    ("balance.py", "m_new = beta * m + (1.0 - beta) * db", "m_new = beta * m + db", "momentum without (1-beta)"),
+    ("balance.py", "b_new = b + m_new", "b_new = b + db", "bias stepped by db, not m"),
+    ("balance.py", "v = (nbar - n) / nbar", "v = (n - nbar) / nbar", "violation sign"),
+    ("balance.py", "np.tanh(kappa * v)", "np.tanh(v)", "dropped kappa"),
+    ("balance.py", "b_new = b_new - b_new.mean()", "b_new = b_new - b.mean()", "sign mode re-centres the old b"),
+    ("balance.py", "m_new = beta * m + (1.0 - beta) * db\n", "m_new = beta * m + (1.0 - beta) * db_raw\n",
+     "re-centre after momentum"),
+    ("balance.py", "db = gamma * np.sign(nbar - n)", "db = gamma * np.sign(nbar - n + 0.5)", "sign(0) taken as +1"),
+    ("loads.py", 'np.argsort(flat, kind="stable")', 'np.argsort(flat, kind="quicksort")', "unstable dispatch"),
+    ("loads.py", "ratio = float(\"inf\") if nmin == 0 else nmax / nmin",
+     "ratio = float(\"inf\") if nmin == 0 else nmax / nbar", "MaxVio over the mean"),
+    ("loads.py", "return ratio, (nmax - nbar) / nbar", "return ratio, (nmax - nmin) / nbar", "excess over min"),
+    ("zloss.py", "lse = (zmax + np.log(", "lse = (np.log(", "dropped max shift"),
+]
+
+
+def _load_mutant(tmp_path, i, fname, old, new):
+    pkg = f"oracle_mutant_{i}"
+    dst = tmp_path / pkg
+    shutil.copytree(ORACLE_DIR, dst, ignore=shutil.ignore_patterns("__pycache__"))
+    path = dst / fname
+    src = path.read_text()
+    assert src.count(old) == 1, f"mutation anchor not unique in {fname}: {old!r}"
+    path.write_text(src.replace(old, new))
+    sys.path.insert(0, str(tmp_path))
+    try:
+        return importlib.import_module(pkg)
+    finally:
+        sys.path.remove(str(tmp_path))
+
+
+@pytest.mark.parametrize("i", range(len(MUTANTS)), ids=[m[3] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, i):
+    fname, old, new, what = MUTANTS[i]
+    mod = _load_mutant(tmp_path, i, fname, old, new)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(mod)
+        except Exception as exc:  # noqa: BLE001 - any failure counts as caught
+            caught.append((pin.__name__, type(exc).__name__))
+    assert caught, f"no pin catches the planted slip: {what}"

@@ -1,0 +1,222 @@
+"""Benchmark: routed tokens/s of the full router step on one MI355X.
+
+One step = router forward (logits, sigmoid, biased Top-4, gates, expert loads) + dispatch
+permutation (for workloads that dispatch) + SMEBU bias update with MaxVio, all on one stream,
+inputs resident in HBM.  Default workload: one GPU's micro-batch share of the Large-style
+step, T = 65536 tokens, d = 3072, N_r = 256, K = 4, 32 Zipf clusters (synthetic).
+
+    python bench.py [--steps K] [--warmup W] [--workload large] [--no-cpu]
+
+Prints one JSON line: throughput, the router kernel's roofline position (algorithmic HBM
+bytes over its own average duration, measured with HIP events on its stream), HBM traffic
+from the committed rocprofv3 counter summary when it matches the current kernel source,
+and the CPU oracle timed on the host on the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, AMD published
+METRIC = "routed tokens/s (logits+top-4+counts+SMEBU) at N_r=256,K=4; % roofline"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "router_mfma_traffic.json")
+KERNEL_SOURCES = ["expert_load_balancing_amd/csrc/router_mfma.hip", "expert_load_balancing_amd/csrc/device_common.hpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def router_alg_bytes(T: int, d: int, n_e: int, k: int) -> int:
+    """HBM bytes the router forward must move: X once, W once, idx + gates out, b in, counts."""
+    return T * (2 * d + 8 * k) + n_e * 2 * d + n_e * 4 + n_e * 4
+
+
+def traffic_from_profile(T: int) -> float | None:
+    """Counter-measured HBM bytes per router launch, if taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash() or rec.get("T") != T:
+        return None
+    return float(rec["traffic_bytes_per_launch"])
+
+
+def cpu_baseline(wl, x, w, b, m, min_seconds: float = 10.0, max_seconds: float = 30.0) -> dict:
+    """The oracle (untuned) on the whole step of the same workload, repeated for >= min_seconds."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    cores = min(16, len(os.sched_getaffinity(0)))
+    with threadpool_limits(limits=cores):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            r = oracle.route(x, w, b, wl.k)
+            n = oracle.expert_loads(r.idx, wl.n_experts)
+            oracle.max_violation(n)
+            if wl.dispatch:
+                oracle.dispatch_permutation(r.idx, wl.n_experts)
+            oracle.balance_step(n, b, m, mode=wl.mode, lam=wl.lam, beta=wl.beta, kappa=wl.kappa, gamma=wl.gamma)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= min_seconds or el * (reps + 1) / reps > max_seconds:
+                break
+    return {"value": reps * wl.T / el, "unit": "routed tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"the full step of {wl.label} (route + loads + MaxVio"
+                      f"{' + dispatch' if wl.dispatch else ''} + {wl.mode} update), {reps} repetition(s), "
+                      f"fp64 numpy, BLAS threads={cores}",
+            "seconds": round(el, 2)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="large")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import datagen
+    import expert_load_balancing_amd as elb
+    from expert_load_balancing_amd import _lib
+
+    wl = datagen.WORKLOADS[args.workload]
+    lib = elb.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    x = datagen.tokens(wl)
+    w = datagen.router_weight(wl)
+    b0, m0 = datagen.initial_bias(wl), datagen.initial_momentum(wl)
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    # Two copies of the tokens, alternated step by step, so no step reads its input out of the
+    # 256 MB last-level cache that the previous step filled.
+    xs = [to_dev(x), to_dev(x)]
+    wd, bd, md = to_dev(w), to_dev(b0), to_dev(m0)
+    T, d, n_e, k = wl.T, wl.d, wl.n_experts, wl.k
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    gates = torch.empty((T, k), dtype=torch.float32, device=dev)
+    counts = torch.empty(n_e, dtype=torch.int32, device=dev)
+    offsets = torch.empty(n_e + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(T * k, dtype=torch.int32, device=dev)
+    inv = torch.empty(T * k, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(16, elb.dispatch_workspace_bytes(T, k, n_e)), dtype=torch.uint8, device=dev)
+    mv = torch.empty(2, dtype=torch.float32, device=dev)
+    dtype_code = elb.ELB_BF16 if wl.dtype == "bf16" else elb.ELB_F32
+    params = _lib.BalanceParams(elb.MODES[wl.mode], wl.lam, wl.beta, wl.kappa, wl.gamma)
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = ctypes.c_void_p
+    xp = [P(t.data_ptr()) for t in xs]
+    wp, bp, mp = P(wd.data_ptr()), P(bd.data_ptr()), P(md.data_ptr())
+    ip, gp, cp = P(idx.data_ptr()), P(gates.data_ptr()), P(counts.data_ptr())
+    op, pp, vp, wsp, mvp = P(offsets.data_ptr()), P(perm.data_ptr()), P(inv.data_ptr()), P(ws.data_ptr()), P(mv.data_ptr())
+    ws_bytes = ws.numel()
+    null = P(0)
+
+    n_ev = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_ev)]
+
+    def step(i: int, timed: bool) -> None:
+        e = ev[i] if timed else None
+        # counts <- 0 (library fill kernel; a T = 0 forward only clears the loads)
+        _lib.check("clear", lib.elb_router_forward(null, dtype_code, 0, d, wp, bp, n_e, k, 0, null, null, cp,
+                                                   null, null, sp))
+        if e:
+            e[0].record(stream)
+        _lib.check("router", lib.elb_router_forward(xp[i & 1], dtype_code, T, d, wp, bp, n_e, k,
+                                                    elb.ELB_ACCUMULATE_COUNTS, ip, gp, cp, null, null, sp))
+        if e:
+            e[1].record(stream)
+        if wl.dispatch:
+            _lib.check("dispatch", lib.elb_router_dispatch(ip, T, k, n_e, wsp, ws_bytes, op, pp, vp, sp))
+        if e:
+            e[2].record(stream)
+        _lib.check("balance", lib.elb_smebu_update(cp, n_e, params, bp, mp, null, mvp, sp))
+        if e:
+            e[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        step(i, True)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    router_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    dispatch_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    balance_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    value = T / (ms * 1e-3)
+
+    alg = router_alg_bytes(T, d, n_e, k)
+    achieved = alg / (router_ms * 1e-3) / 1e9
+    flops = 2.0 * T * d * n_e
+    tflops = flops / (router_ms * 1e-3) / 1e12
+    traffic = traffic_from_profile(T)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "routed tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.label, "T": T, "d": d, "n_experts": n_e, "k": k, "balance": wl.mode,
+                   "dispatch": wl.dispatch, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else round(traffic),
+                     "kernel": "router_mfma_kernel<4>", "alg_bytes_per_launch": alg,
+                     "kernel_us": round(router_ms * 1e3, 2),
+                     "mfma_tflops": round(tflops, 1), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)},
+        "breakdown_us": {"router": round(router_ms * 1e3, 2), "dispatch": round(dispatch_ms * 1e3, 2),
+                         "balance": round(balance_ms * 1e3, 2), "step": round(ms * 1e3, 2)},
+        "maxvio_last": float(mv.cpu()[0]),
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(wl, x, w, b0, m0)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

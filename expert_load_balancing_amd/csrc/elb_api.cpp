@@ -1,0 +1,102 @@
+// C-ABI entry points of libelb: argument checks, then kernel selection and launch.
+// Every check happens before anything is queued; see include/elb.h for the contract.
+#include "../../include/elb.h"
+
+#include "elb_kernels.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+elb_status from_hip(hipError_t e) { return e == hipSuccess ? ELB_OK : ELB_ERR_LAUNCH; }
+
+constexpr uint32_t kKnownFlags = ELB_GATES_RAW | ELB_ACCUMULATE_COUNTS | ELB_FORCE_GENERIC;
+
+}  // namespace
+
+extern "C" {
+
+elb_status elb_router_forward(const void* x, int32_t dtype, int64_t T, int32_t d, const void* w, const float* bias,
+                              int32_t n_experts, int32_t k, uint32_t flags, int32_t* topk_idx, float* gates,
+                              int32_t* counts, float* logits, float* lse, elb_stream_t stream) {
+  if (w == nullptr || bias == nullptr || counts == nullptr) return ELB_ERR_NULL;
+  if (T > 0 && (x == nullptr || topk_idx == nullptr || gates == nullptr)) return ELB_ERR_NULL;
+  if (dtype != ELB_F32 && dtype != ELB_BF16) return ELB_ERR_UNSUPPORTED;
+  if (flags & ~kKnownFlags) return ELB_ERR_UNSUPPORTED;
+  if (T < 0 || d < 1 || n_experts < 1 || n_experts > 256 || k < 1 || k > 8 || k > n_experts) return ELB_ERR_SHAPE;
+  if (T * (int64_t)k >= (int64_t(1) << 31) || T * (int64_t)n_experts >= (int64_t(1) << 62)) return ELB_ERR_SHAPE;
+  const int64_t elem = dtype == ELB_F32 ? 4 : 2;
+  if ((d * elem) % 16 != 0 || !aligned(w, 16)) return ELB_ERR_ALIGN;
+  if (T > 0 && (!aligned(x, 16) || !aligned(topk_idx, 16) || !aligned(gates, 16))) return ELB_ERR_ALIGN;
+  if (!aligned(bias, 4) || !aligned(counts, 4) || !aligned(logits, 4) || !aligned(lse, 4)) return ELB_ERR_ALIGN;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (!(flags & ELB_ACCUMULATE_COUNTS)) {
+    const hipError_t err = elb::launch_fill_i32(counts, n_experts, 0, s);
+    if (err != hipSuccess) return ELB_ERR_LAUNCH;
+  }
+  if (T == 0) return ELB_OK;
+  const elb::RouterArgs a{x, dtype, T, d, w, bias, n_experts, k, flags, topk_idx, gates, counts, logits, lse};
+  if (!(flags & ELB_FORCE_GENERIC) && elb::router_mfma_applies(a)) return from_hip(elb::launch_router_mfma(a, s));
+  return from_hip(elb::launch_router_generic(a, s));
+}
+
+size_t elb_dispatch_workspace_bytes(int64_t T, int32_t k, int32_t n_experts) {
+  if (T < 0 || k < 1 || k > 8 || n_experts < 1 || n_experts > 256) return 0;
+  if (T * (int64_t)k >= (int64_t(1) << 31)) return 0;
+  return elb::dispatch_workspace_bytes(T * (int64_t)k, n_experts);
+}
+
+elb_status elb_router_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t n_experts, void* workspace,
+                               size_t workspace_bytes, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                               elb_stream_t stream) {
+  if (offsets == nullptr) return ELB_ERR_NULL;
+  if (T > 0 && (topk_idx == nullptr || perm == nullptr || workspace == nullptr)) return ELB_ERR_NULL;
+  if (T < 0 || k < 1 || k > 8 || n_experts < 1 || n_experts > 256) return ELB_ERR_SHAPE;
+  if (T * (int64_t)k >= (int64_t(1) << 31)) return ELB_ERR_SHAPE;
+  if (workspace_bytes < elb::dispatch_workspace_bytes(T * (int64_t)k, n_experts)) return ELB_ERR_WORKSPACE;
+  if (!aligned(topk_idx, 4) || !aligned(offsets, 4) || !aligned(perm, 4) || !aligned(inv_perm, 4) ||
+      !aligned(workspace, 16))
+    return ELB_ERR_ALIGN;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return from_hip(elb::launch_dispatch(topk_idx, T * (int64_t)k, n_experts, workspace, offsets, perm, inv_perm, s));
+}
+
+elb_status elb_smebu_update(const int32_t* counts, int32_t n_experts, elb_balance_params params, float* bias,
+                            float* momentum, float* delta_b, float* maxvio, elb_stream_t stream) {
+  if (params.mode != ELB_MODE_SMEBU && params.mode != ELB_MODE_SIGN && params.mode != ELB_MODE_LINEAR)
+    return ELB_ERR_UNSUPPORTED;
+  if (counts == nullptr || bias == nullptr) return ELB_ERR_NULL;
+  if (params.mode != ELB_MODE_SIGN && momentum == nullptr) return ELB_ERR_NULL;
+  if (n_experts < 1 || n_experts > 1024) return ELB_ERR_SHAPE;
+  if (!aligned(counts, 4) || !aligned(bias, 4) || !aligned(momentum, 4) || !aligned(delta_b, 4) || !aligned(maxvio, 4))
+    return ELB_ERR_ALIGN;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return from_hip(elb::launch_balance(counts, n_experts, params.mode, params.lambda, params.beta, params.kappa,
+                                      params.gamma, bias, momentum, delta_b, maxvio, s));
+}
+
+elb_status elb_maxvio(const int32_t* counts, int32_t n_experts, float* out, elb_stream_t stream) {
+  if (counts == nullptr || out == nullptr) return ELB_ERR_NULL;
+  if (n_experts < 1 || n_experts > 1024) return ELB_ERR_SHAPE;
+  if (!aligned(counts, 4) || !aligned(out, 4)) return ELB_ERR_ALIGN;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return from_hip(elb::launch_balance(counts, n_experts, -1, 0.f, 0.f, 0.f, 0.f, nullptr, nullptr, nullptr, out, s));
+}
+
+const char* elb_status_str(elb_status status) {
+  switch (status) {
+    case ELB_OK: return "ok";
+    case ELB_ERR_NULL: return "a required pointer is NULL";
+    case ELB_ERR_SHAPE: return "a size is outside the supported range";
+    case ELB_ERR_UNSUPPORTED: return "unknown dtype, mode or flag";
+    case ELB_ERR_ALIGN: return "a pointer or row is not aligned as required";
+    case ELB_ERR_WORKSPACE: return "workspace smaller than elb_dispatch_workspace_bytes";
+    case ELB_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
+  }
+  return "unknown status";
+}
+
+int elb_version(void) { return ELB_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,161 @@
+/*
+ * elb.h - sigmoid Top-K MoE router and expert-bias load balancing on one MI355X (gfx950).
+ *
+ * C ABI.  Every array argument is a DEVICE pointer owned by the caller; the library never
+ * allocates, frees or keeps memory or state between calls.  Every call is asynchronous on
+ * `stream` (a hipStream_t; NULL means the default stream) and returns as soon as its
+ * kernels are queued.  Arguments are checked synchronously, before any launch: a bad
+ * argument returns an error code and queues nothing.  Faults inside a kernel surface at
+ * the caller's next synchronisation, as usual in HIP.  No C++ exception crosses the ABI.
+ * All functions are thread-safe and re-entrant (no global mutable state).
+ *
+ * What is computed, per token t and routed expert i (N_r = n_experts):
+ *   z_{t,i} = u_t . e_i                      router logit (no bias term)
+ *   s_{t,i} = 1 / (1 + exp(-z_{t,i}))        sigmoid score, per expert, not normalised
+ *   the K experts with the largest s_{t,i} + b_i are chosen; the bias is used only for
+ *   this choice, and the gates come from s alone.
+ *   [SMEBU Load Balancing (AI Engineer Exhaustive study note), "How it works", eq. (17);
+ *    Arcee Trinity Large Technical Report (paperlayer.ai summary), section 2.3;
+ *    hotdry blog post on Trinity Large MoE routing, section on sigmoid routing and Top-K]
+ * and once per optimizer step the bias b is moved towards balanced expert loads n_i by
+ * SMEBU (eq. (23)-(28) of the study note), or by the Nano/Mini sign step (eq. (20)-(22)),
+ * or by the unclamped linear step the note contrasts them with.
+ */
+#ifndef ELB_H
+#define ELB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ELB_VERSION 10000 /* major * 10000 + minor * 100 + patch */
+
+typedef struct ihipStream_t* elb_stream_t; /* hipStream_t; NULL = default stream */
+
+typedef enum {
+  ELB_OK = 0,
+  ELB_ERR_NULL = 1,        /* a required pointer is NULL                         */
+  ELB_ERR_SHAPE = 2,       /* a size is outside the supported range              */
+  ELB_ERR_UNSUPPORTED = 3, /* unknown dtype, mode or flag bit                    */
+  ELB_ERR_ALIGN = 4,       /* a pointer or row is not 16-byte aligned            */
+  ELB_ERR_WORKSPACE = 5,   /* workspace smaller than elb_dispatch_workspace_bytes */
+  ELB_ERR_LAUNCH = 6       /* the HIP runtime refused a launch (e.g. wrong GPU)  */
+} elb_status;
+
+typedef enum { ELB_F32 = 0, ELB_BF16 = 1 } elb_dtype;
+
+typedef enum {
+  ELB_MODE_SMEBU = 0,  /* eq. (23)-(28): tanh-clamped, re-centred, with momentum       */
+  ELB_MODE_SIGN = 1,   /* eq. (20)-(22): gamma * sign(nbar - n_i), then re-centre b     */
+  ELB_MODE_LINEAR = 2  /* SMEBU with the clamp removed: db_i = lambda * v_i            */
+} elb_mode;
+
+/* Flags of elb_router_forward. */
+enum {
+  ELB_GATES_RAW = 1u << 0,         /* gates = s of the chosen experts, instead of s divided
+                                      by its sum over the K chosen (the default)              */
+  ELB_ACCUMULATE_COUNTS = 1u << 1, /* add this batch's loads into `counts` (several
+                                      micro-batches per optimizer step) instead of
+                                      overwriting them                                      */
+  ELB_FORCE_GENERIC = 1u << 2      /* use the shape-generic kernel even where the MFMA
+                                      kernel applies (tests compare the two)                 */
+};
+
+typedef struct {
+  int32_t mode; /* elb_mode                                                       */
+  float lambda; /* SMEBU / linear step size (Trinity Large: 5e-4)                   */
+  float beta;   /* momentum factor (Trinity Large: 0.5)                             */
+  float kappa;  /* tanh slope (Trinity Large: 2)                                    */
+  float gamma;  /* sign-step size                                                   */
+} elb_balance_params;
+
+/*
+ * Router forward for one batch of tokens.
+ *   x        [T, d] hidden states u_t, row-major, elements of `dtype` (fp32 or bf16).
+ *   w        [n_experts, d] router weight rows e_i (expert centroids), row-major, `dtype`.
+ *   bias     [n_experts] fp32 expert bias b_i.
+ *   topk_idx [T, k] int32 out: chosen experts, in descending s + b; equal values go to the
+ *            lower expert index.
+ *   gates    [T, k] fp32 out: s of the chosen experts divided by their sum over the k
+ *            chosen ("normalized scores", report section 2.3), or s itself with
+ *            ELB_GATES_RAW.  Never depends on b.
+ *   counts   [n_experts] int32 in/out: n_i, the number of (token, slot) pairs routed to
+ *            expert i.  Overwritten unless ELB_ACCUMULATE_COUNTS is set.
+ *   logits   [T, n_experts] fp32 out, or NULL: z_{t,i} (a parity aid; costs bandwidth).
+ *   lse      [T] fp32 out, or NULL: log sum_i exp(z_{t,i}), the per-token term of the
+ *            router z-loss (talk summary "Arcee Halts 400B Blackwell Model Collapse...",
+ *            section "Precision Fallbacks, Loss Stabilization, and MaxVio ...").
+ * Supported: 0 <= T, T * k < 2^31; 1 <= k <= min(8, n_experts); n_experts <= 256;
+ * d >= 1 with every row 16-byte aligned (d % 8 == 0 for bf16, d % 4 == 0 for fp32);
+ * x and w 16-byte aligned.  bf16 inputs with d % 64 == 0 run on the MFMA kernel.
+ * Inputs must be finite.  Errors: ELB_ERR_NULL, ELB_ERR_SHAPE, ELB_ERR_ALIGN,
+ * ELB_ERR_UNSUPPORTED (dtype or flag), ELB_ERR_LAUNCH.
+ */
+elb_status elb_router_forward(const void* x, int32_t dtype, int64_t T, int32_t d, const void* w,
+                              const float* bias, int32_t n_experts, int32_t k, uint32_t flags,
+                              int32_t* topk_idx, float* gates, int32_t* counts, float* logits,
+                              float* lse, elb_stream_t stream);
+
+/*
+ * Bytes of device workspace elb_router_dispatch needs for these sizes (0 when T == 0).
+ * Errors are reported as 0 only when the sizes are themselves invalid.
+ */
+size_t elb_dispatch_workspace_bytes(int64_t T, int32_t k, int32_t n_experts);
+
+/*
+ * Counting-sort dispatch of the flat assignments j = t * k + slot by expert (the pages
+ * define none; this is the plain stable counting sort):
+ *   offsets  [n_experts + 1] int32 out: bucket e is perm[offsets[e] .. offsets[e+1]).
+ *   perm     [T * k] int32 out: flat positions j, grouped by expert, ascending within each
+ *            expert.
+ *   inv_perm [T * k] int32 out, or NULL: perm[inv_perm[j]] == j.
+ *   workspace: device memory of at least elb_dispatch_workspace_bytes(T, k, n_experts)
+ *            bytes, 16-byte aligned; its contents on entry do not matter.
+ * topk_idx entries must lie in [0, n_experts).  Errors: ELB_ERR_NULL, ELB_ERR_SHAPE,
+ * ELB_ERR_WORKSPACE, ELB_ERR_ALIGN, ELB_ERR_LAUNCH.
+ */
+elb_status elb_router_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t n_experts,
+                               void* workspace, size_t workspace_bytes, int32_t* offsets,
+                               int32_t* perm, int32_t* inv_perm, elb_stream_t stream);
+
+/*
+ * One expert-bias update from one optimizer step's loads (study note eq. (20)-(28)).
+ *   counts   [n_experts] int32: n_i for the step.
+ *   bias     [n_experts] fp32 in/out: b.
+ *   momentum [n_experts] fp32 in/out: m (SMEBU and linear modes; untouched by SIGN).
+ *   delta_b  [n_experts] fp32 out, or NULL: the applied step (re-centred db for SMEBU and
+ *            LINEAR, gamma * sign(nbar - n_i) for SIGN).
+ *   maxvio   [2] fp32 out, or NULL: {max n / min n, (max n - nbar) / nbar} of `counts`.
+ * SMEBU:  v = (nbar - n) / nbar; db = lambda * tanh(kappa * v); db -= mean(db);
+ *         m = beta * m + (1 - beta) * db; b += m.
+ * SIGN:   b += gamma * sign(nbar - n); b -= mean(b).
+ * LINEAR: as SMEBU with tanh(kappa * v) replaced by v.
+ * When every count is 0 the step is skipped (b, m unchanged, delta_b = 0, maxvio NaN).
+ * Supported: 1 <= n_experts <= 1024.  Errors: ELB_ERR_NULL, ELB_ERR_SHAPE,
+ * ELB_ERR_UNSUPPORTED (mode), ELB_ERR_LAUNCH.
+ */
+elb_status elb_smebu_update(const int32_t* counts, int32_t n_experts, elb_balance_params params,
+                            float* bias, float* momentum, float* delta_b, float* maxvio,
+                            elb_stream_t stream);
+
+/*
+ * MaxVio of one step's loads: out[0] = max n / min n (the talk's definition, section
+ * "The MaxVio Metric and the Day-4 Crisis"; +inf when an expert got nothing), out[1] =
+ * (max n - nbar) / nbar.  Both NaN when every count is 0.  Supported: 1 <= n_experts <= 1024.
+ */
+elb_status elb_maxvio(const int32_t* counts, int32_t n_experts, float* out, elb_stream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char* elb_status_str(elb_status status);
+
+/* ELB_VERSION of the built library. */
+int elb_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ELB_H */

@@ -1,0 +1,162 @@
+"""GPU parity of the router forward against the oracle, element by element, on shapes the
+oracle finishes in seconds: several 256-token tiles, ragged tails, every K, padded expert
+counts, exact ties, duplicate tokens, empty batches and count accumulation."""
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import expert_load_balancing_amd as elb
+import oracle
+from gpu_util import compare_logits, compare_route, check_counts, log, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def make(T, d, n_e, k, dtype="bf16", seed=7, kind="clusters"):
+    wl = datagen.WORKLOADS["large"].replace(T=T, d=d, n_experts=n_e, k=k, dtype=dtype, seed=seed, token_kind=kind,
+                                            n_clusters=8 if kind == "clusters" else 0)
+    return wl, datagen.tokens(wl), datagen.router_weight(wl), datagen.initial_bias(wl)
+
+
+def run(x, w, b, k, **kw):
+    res = elb.router_forward(to_dev(x), to_dev(w), to_dev(b), k, want_logits=True, **kw)
+    torch.cuda.synchronize()
+    return [t.cpu().numpy() for t in res]
+
+
+@pytest.mark.parametrize("T,d,n_e,k,kind", [
+    (1000, 256, 256, 4, "clusters"),   # 4 tiles, ragged tail of 232
+    (256, 512, 256, 4, "iid"),         # exactly one tile
+    (777, 320, 256, 1, "iid"),
+    (513, 192, 256, 2, "clusters"),
+    (300, 128, 256, 3, "iid"),
+    (640, 256, 256, 8, "clusters"),
+    (450, 256, 200, 4, "iid"),         # padded experts (200 of 256)
+    (129, 64, 16, 2, "iid"),           # tiny expert count, d = one stage
+    (2048, 1024, 256, 4, "clusters"),
+])
+@pytest.mark.parametrize("kernel", ["mfma", "generic"])
+def test_router_matches_oracle(T, d, n_e, k, kind, kernel):
+    log(f"router parity kernel={kernel} T={T} d={d} N_r={n_e} K={k} tokens={kind}")
+    wl, x, w, b = make(T, d, n_e, k, kind=kind)
+    idx, gates, counts, logits = run(x, w, b, k, force_generic=(kernel == "generic"))
+    rep = compare_route(idx, gates, x, w, b, k)
+    check_counts(counts, idx, n_e)
+    err = compare_logits(logits, x, w)
+    log(f"  ties={rep.ties} (mismatched {rep.tie_mismatch}) order-ties={rep.order_ties} "
+        f"gate rel err={rep.max_gate_rel:.2e} logit abs err={err:.2e}")
+
+
+def test_fp32_tiny_workload():
+    wl = datagen.WORKLOADS["tiny"]
+    x, w, b = datagen.tokens(wl), datagen.router_weight(wl), datagen.initial_bias(wl)
+    log(f"fp32 workload {wl.label}")
+    idx, gates, counts, logits = run(x, w, b, wl.k)
+    rep = compare_route(idx, gates, x, w, b, wl.k)
+    check_counts(counts, idx, wl.n_experts)
+    err = compare_logits(logits, x, w)
+    assert err < 1e-5, err  # fp32 inputs keep fp32-exact logits
+    log(f"  ties={rep.ties} gate rel err={rep.max_gate_rel:.2e} logit err={err:.2e}")
+
+
+@pytest.mark.parametrize("kernel", ["mfma", "generic"])
+def test_raw_gates(kernel):
+    wl, x, w, b = make(600, 256, 256, 4)
+    idx, gates, counts, _ = run(x, w, b, 4, gates_raw=True, force_generic=(kernel == "generic"))
+    compare_route(idx, gates, x, w, b, 4, normalize=False)
+
+
+@pytest.mark.parametrize("kernel", ["mfma", "generic"])
+def test_exact_ties_go_to_the_lower_index(kernel):
+    """Experts 37 and 200 get identical weight rows and bias: identical s + b in every token.
+    Wherever that pair is chosen, 37 must come first; where only one fits, it must be 37."""
+    wl, x, w, b = make(512, 256, 256, 4, kind="iid")
+    w = w.copy()
+    b = b.copy()
+    w[200] = w[37]
+    b[200] = b[37]
+    # make the pair attractive so it is chosen often
+    b[37] = b[200] = np.float32(b.max() + 0.05)
+    idx, gates, counts, _ = run(x, w, b, 4, force_generic=(kernel == "generic"))
+    has37 = (idx == 37).any(1)
+    has200 = (idx == 200).any(1)
+    assert has37.sum() > 100
+    assert not (has200 & ~has37).any(), "expert 200 chosen without its lower-index twin 37"
+    both = has37 & has200
+    pos37 = np.argmax(idx == 37, axis=1)
+    pos200 = np.argmax(idx == 200, axis=1)
+    assert (pos37[both] < pos200[both]).all()
+    compare_route(idx, gates, x, w, b, 4)
+
+
+@pytest.mark.parametrize("kernel", ["mfma", "generic"])
+def test_duplicate_tokens_route_identically(kernel):
+    wl, x, w, b = make(1024, 256, 256, 4)
+    x = x.copy()
+    src = np.array([3, 3, 500, 900])
+    dst = np.array([700, 1023, 255, 256])  # across tiles, waves and lane halves
+    x[dst] = x[src]
+    idx, gates, _, logits = run(x, w, b, 4, force_generic=(kernel == "generic"))
+    assert (idx[dst] == idx[src]).all()
+    assert (gates[dst].view(np.uint32) == gates[src].view(np.uint32)).all()
+    assert (logits[dst].view(np.uint32) == logits[src].view(np.uint32)).all()
+
+
+def test_mfma_and_generic_agree():
+    wl, x, w, b = make(1500, 512, 256, 4)
+    i1, g1, c1, z1 = run(x, w, b, 4)
+    i2, g2, c2, z2 = run(x, w, b, 4, force_generic=True)
+    r = oracle.route(x, w, b, 4)
+    decided = r.gap >= 1e-3
+    assert (i1[decided] == i2[decided]).all()
+    assert np.allclose(z1, z2, rtol=1e-4, atol=1e-4)
+
+
+@pytest.mark.parametrize("kernel", ["mfma", "generic"])
+def test_empty_batch_and_accumulation(kernel):
+    dev = "cuda"
+    wl, x, w, b = make(300, 256, 256, 4)
+    xd, wd, bd = to_dev(x), to_dev(w), to_dev(b)
+    counts = torch.full((256,), 123, dtype=torch.int32, device=dev)
+    elb.router_forward(xd[:0], wd, bd, 4, counts=counts, force_generic=(kernel == "generic"))
+    torch.cuda.synchronize()
+    assert int(counts.abs().sum()) == 0, "empty batch must leave zero counts"
+    idx1, _, _ = elb.router_forward(xd[:100], wd, bd, 4, counts=counts, force_generic=(kernel == "generic"))
+    idx2, _, _ = elb.router_forward(xd[100:], wd, bd, 4, counts=counts, accumulate=True,
+                                    force_generic=(kernel == "generic"))
+    torch.cuda.synchronize()
+    both = np.concatenate([idx1.cpu().numpy(), idx2.cpu().numpy()])
+    check_counts(counts.cpu().numpy(), both, 256)
+    assert int(counts.sum()) == 300 * 4
+
+
+@pytest.mark.parametrize("kernel", ["mfma", "generic"])
+def test_lse_for_router_z_loss(kernel):
+    wl, x, w, b = make(700, 256, 256, 4)
+    res = elb.router_forward(to_dev(x), to_dev(w), to_dev(b), 4, want_lse=True, force_generic=(kernel == "generic"))
+    torch.cuda.synchronize()
+    lse = res[3].cpu().numpy().astype(np.float64)
+    _, want = oracle.router_z_loss(oracle.router_logits(x, w))
+    assert np.allclose(lse, want, rtol=1e-5, atol=1e-5), np.abs(lse - want).max()
+
+
+def test_bias_shift_leaves_routing_unchanged():
+    """Adding one constant to every b_i changes no choice and no gate (gates never see b)."""
+    wl, x, w, b = make(800, 256, 256, 4)
+    i1, g1, c1, _ = run(x, w, b, 4)
+    i2, g2, c2, _ = run(x, w, (b + np.float32(0.25)).astype(np.float32), 4)
+    r = oracle.route(x, w, b, 4)
+    decided = r.gap >= 1e-3
+    assert (i1[decided] == i2[decided]).all()
+    same = (i1 == i2).all(1)
+    assert np.allclose(g1[same], g2[same], rtol=1e-6, atol=0)
+
+
+def test_determinism():
+    wl, x, w, b = make(3000, 512, 256, 4)
+    a = run(x, w, b, 4)
+    c = run(x, w, b, 4)
+    for u, v in zip(a, c):
+        assert (u.view(np.uint32) == v.view(np.uint32)).all()

@@ -18,22 +18,30 @@
 //   logits of each of its tokens, and the other 128 sit in lane ^ 32.  Top-K therefore needs
 //   no LDS round trip: a register-local selection over 128 values, then one cross-lane merge.
 //
-// Memory pipeline (per 64-element slice of d, "stage"):
-//   global -> VGPR (16-byte buffer loads, 8 consecutive lanes read one 128-byte row segment,
-//   so every HBM line is fully used; rows past T or past N_r come back as zeros from the
-//   buffer range check) -> LDS (two stages, rows XOR-swizzled in 16-byte chunks so both the
-//   stores and the MFMA operand reads are bank-conflict free) -> MFMA operands.
-//   The loads for stage k+2 are issued right after stage k+1 is written to LDS, so they fly
-//   during the 64 MFMAs of stage k+1; barriers fence LDS only (see lds_barrier).
+// Memory pipeline: d is consumed in stages of 64 elements (128 bytes of every row: every
+//   tile row costs HBM one full line per visit; 64-byte visits stream markedly slower because
+//   all workgroups touch 256 rows 2*d bytes apart at once).  Rows go from HBM (tokens) or L2
+//   (router weights) straight into LDS with buffer-to-LDS DMA loads, which need no registers:
+//   the token stream runs 2 stages ahead in a ring of 3 LDS slots, the weight stream 1 stage
+//   ahead in a ring of 2 (weights come from L2, well within one stage).  The five 32 KiB slots
+//   fill the 160 KiB LDS.  Rows past T or past N_r fall outside the buffer range and arrive as
+//   zeros.  Every wave waits for its own DMAs with an explicit vmcnt budget, then one barrier
+//   per stage publishes the slot to all waves and frees the slot the next DMA overwrites.
+//   Barriers carry no memory fence: a fence on LDS would wait for every DMA in flight and
+//   drain the prefetch.  Near the end, out-of-range dummy DMAs keep the vmcnt budget uniform;
+//   they move no HBM bytes.  Within a slot, the eight 16-byte chunks of row r sit at
+//   chunk ^ ((r >> 1) & 7), which keeps the MFMA operand reads (16 rows x 16 bytes per LDS
+//   cycle over 64 banks) free of bank conflicts.
 //
 // Epilogue (per lane, per token): s = 1 / (1 + 2^(-z log2 e)) with the hardware exp2/rcp;
-//   the selection key is the fp32 bit pattern of s + b' with its low 8 bits replaced by
-//   255 - i, where b' = b + (1 - min b) >= 1 keeps every key a positive float, so float
-//   max / med3 order keys exactly like (s + b, -i).  Keeping 24 bits of s + b' resolves
-//   differences down to 2^-15 (1 + max b - min b); closer calls fall to the lower index.
-//   Insertion into a sorted top-K list is one max plus K-1 med3.  The chosen experts' exact
-//   scores come back through LDS for the gates.  Loads: LDS histogram, one global atomic per
-//   expert per workgroup.
+//   the selection key is the fp32 bit pattern of s + b' with its low 8 bits replaced by an
+//   index, where b' = b + (1 - min b) >= 1 keeps every key a positive float, so float max and
+//   med3 order keys exactly like (s + b, -index).  Inside a lane the index is the lane-local
+//   slot (ascending with the expert id); the K survivors are re-keyed with 255 - expert before
+//   the cross-lane merge.  Keeping 24 bits of s + b' resolves differences down to
+//   2^-15 (1 + max b - min b); closer calls go to the lower index.  Insertion into a sorted
+//   top-K list is one max plus K-1 med3.  The chosen experts' exact scores come back through
+//   LDS for the gates.  Loads: LDS histogram, one global atomic per expert per workgroup.
 #include "device_common.hpp"
 #include "elb_kernels.h"
 
@@ -46,35 +54,64 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
-typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
-constexpr int kExp = 256;                        // experts per tile (padded)
-constexpr int kMB = kExp / 32;                   // 32-row MFMA blocks of experts
-constexpr int kTokWave = 64;                     // tokens per wave
-constexpr int kNB = kTokWave / 32;               // 32-column MFMA blocks of tokens
-constexpr int kTile = kWaves * kTokWave;         // tokens per workgroup
-constexpr int kBK = 64;                          // d elements per stage
-constexpr int kRowB = kBK * 2;                   // bytes of one row per stage
-constexpr int kWBytes = kExp * kRowB;            // 32 KiB
-constexpr int kXBytes = kTile * kRowB;           // 32 KiB
-constexpr int kStage = kWBytes + kXBytes;        // 64 KiB
-constexpr int kLoads = kWBytes / (kThreads * 16);  // 16-byte loads per thread per tensor
-constexpr int kRowsPerLoad = kThreads / 8;       // rows covered by one load instruction (32)
+constexpr int kExp = 256;                 // experts per tile (padded)
+constexpr int kMB = kExp / 32;            // 32-row MFMA blocks of experts
+constexpr int kTokWave = 64;              // tokens per wave
+constexpr int kNB = kTokWave / 32;        // 32-column MFMA blocks of tokens
+constexpr int kTile = kWaves * kTokWave;  // tokens per workgroup
+constexpr int kBK = 64;                   // d elements per stage
+constexpr int kRowB = kBK * 2;            // bytes of one row per stage
+constexpr int kSlot = 256 * kRowB;        // one stage of 256 rows: 32 KiB
+constexpr int kNX = 3, kPX = 2;           // token ring: slots, stages in flight
+constexpr int kNW = 2, kPW = 1;           // weight ring
+constexpr int kUnroll = 6;                // lcm(kNX, kNW): slots are compile-time constants
+constexpr int kKSteps = kBK / 16;         // MFMA k-steps per stage
+// The compiler tracks at most 8 distinct LDS DMA targets when it decides which DMAs an LDS
+// read must wait for; with more slots it would fall back to waiting for all of them.
+static_assert(kNX + kNW <= 8, "at most 8 DMA target slots");
+static_assert((kNX + kNW) * kSlot <= 160 * 1024, "LDS");
+constexpr int kDma = kSlot / (kWaves * 1024);  // DMA instructions per wave per slot (1 KiB each)
+constexpr uint32_t kOOB = 0x7FFFFF00u;    // voffset outside every buffer: dummy DMA
 constexpr float kLog2e = 1.4426950408889634f;
 
-static_assert(kLoads * kRowsPerLoad == kExp && kXBytes == kWBytes, "load mapping");
-static_assert(kWaves * 32768 <= 2 * kStage, "per-wave score slices must fit in the stage buffers");
+static_assert(kNX == kPX + 1 && kNW == kPW + 1 && kUnroll % kNX == 0 && kUnroll % kNW == 0, "ring shape");
+static_assert(kPX >= kPW, "the vmcnt budget below assumes the token stream runs further ahead");
+// VMEM instructions a wave issues after the DMAs of stage j's weights, when it must have stage j:
+// the token DMAs of the same iteration, then (kPW - 1) full iterations.
+constexpr int kVmBudget = kDma + 2 * kDma * (kPW - 1);
+
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitLgkm0 = 63 & 15 | (3 << 14) | (7 << 4);  // lgkmcnt(0) only
+
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   // Raw buffer: stride 0, range checked against `bytes`; out-of-range loads return zeros.
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0);
+#define ELB_AS3(p) ((__attribute__((address_space(3))) void*)(p))
+
+// One wave's share of one slot: kDma 1-KiB DMA instructions (8 rows each).
+__device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, unsigned char* wave_base, const uint32_t (&vo)[kDma],
+                                         uint32_t soff, bool real) {
+#pragma unroll
+  for (int i = 0; i < kDma; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, ELB_AS3(wave_base + i * 1024), 16, real ? vo[i] : kOOB, (int)soff, 0, 0);
 }
+
+// LDS position of 16-byte chunk c of a 128-byte row segment r.  The LDS serves 16 lanes x 16
+// bytes per cycle from 64 banks; an MFMA operand read has 16 consecutive rows read the same
+// chunk, and XOR-ing the chunk with bits 1..3 of the row spreads those 16 reads over the
+// whole 256-byte bank window (rows r and r + 1 already sit in different 128-byte halves).
+__device__ __forceinline__ constexpr int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 // Sorted (descending) top-K insertion: the new j-th largest is med3(old (j-1)-th, old j-th, x).
 template <int K>
@@ -88,67 +125,66 @@ __device__ __forceinline__ float sigmoid_fast(float z) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
 }
 
-template <int K, bool EXTRA>
+template <int K, bool FULL, bool EXTRA>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void router_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const float* __restrict__ bias, int64_t T, int d,
     int n_experts, int normalize, int32_t* __restrict__ idx_out, float* __restrict__ gates_out,
     int32_t* __restrict__ counts, float* __restrict__ logits, float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kStage];
-  __shared__ __attribute__((aligned(16))) float bprime[kExp];
-  __shared__ int hist[kExp];
-  __shared__ float wave_min[kWaves];
+  // The five ring slots are the whole LDS; the epilogue reuses them once the ring drains.
+  __shared__ __attribute__((aligned(1024))) unsigned char xs0[kSlot], xs1[kSlot], xs2[kSlot];
+  __shared__ __attribute__((aligned(1024))) unsigned char ws0[kSlot], ws1[kSlot];
+  auto xslot = [&](int i) -> unsigned char* { return i == 0 ? xs0 : i == 1 ? xs1 : xs2; };
+  auto wslot = [&](int i) -> unsigned char* { return i == 0 ? ws0 : ws1; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps LDS bases in SGPRs
   const int h = lane >> 5;
   const int l32 = lane & 31;
   const int64_t row0 = (int64_t)blockIdx.x * kTile;
   const int rows = (int)(T - row0 < kTile ? T - row0 : kTile);
+  const int nkb = d / kBK;
 
-  // ---- shifted bias b' = b + (1 - min b) >= 1, so every selection key is a positive float ----
-  const float bv = tid < n_experts ? bias[tid] : __builtin_inff();
-  float mn = bv;
+  // Bias loads go first: a load issued behind the DMA prologue would have to wait for it.
+  // Each wave reads all of b (4 values per lane) to form min b without any LDS.
+  float bq[4];
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) mn = fminf(mn, __shfl_xor(mn, off));
-  if (lane == 0) wave_min[wave] = mn;
-  hist[tid] = 0;
-  lds_barrier();
-  const float shift = 1.0f - fminf(fminf(wave_min[0], wave_min[1]), fminf(wave_min[2], wave_min[3]));
-  bprime[tid] = tid < n_experts ? bv + shift : 0.0f;  // visible after the first main-loop barrier
+  for (int c = 0; c < 4; ++c) bq[c] = lane + 64 * c < n_experts ? bias[lane + 64 * c] : __builtin_inff();
 
-  // ---- operand streams ----
+  // ---- operand streams: start the DMA ring ----
   const uint32_t row_bytes = (uint32_t)d * 2u;
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + row0 * d, (uint32_t)rows * row_bytes);
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, (uint32_t)n_experts * row_bytes);
-  const int lrow = tid >> 3;  // row within a 32-row group
-  const int lc = tid & 7;     // 16-byte chunk within the 128-byte row segment
-  const uint32_t goff = (uint32_t)lrow * row_bytes + (uint32_t)lc * 16u;
-  const uint32_t gstep = (uint32_t)kRowsPerLoad * row_bytes;
-  const uint32_t soff = (uint32_t)lrow * kRowB + (uint32_t)((lc ^ (lrow & 7)) << 4);
-  constexpr uint32_t sstep = kRowsPerLoad * kRowB;  // 4 KiB
+  // DMA lane mapping: instruction i of wave `wave` fills rows wave*64 + 8 i + lane/8; lane
+  // position p = lane & 7 in the row receives the global chunk stored there, swz(row, p)
+  // (the swizzle is its own inverse).
+  uint32_t vo[kDma];
+#pragma unroll
+  for (int i = 0; i < kDma; ++i) {
+    const int r = wave * 64 + 8 * i + (lane >> 3);
+    vo[i] = (uint32_t)r * row_bytes + (uint32_t)(swz(r, lane & 7) << 4);
+  }
+  const uint32_t wave_off = (uint32_t)wave * (64 * kRowB);
+  // Prologue: stages 0..kPX-1 of the tokens and 0..kPW-1 of the weights, issued in the same
+  // order the steady state uses (weights first, then tokens, per virtual iteration).
+#pragma unroll
+  for (int vi = -kPX; vi < 0; ++vi) {
+    if (vi + kPW >= 0) dma_rows(wr, wslot((vi + kPW) % kNW) + wave_off, vo, (uint32_t)(vi + kPW) * kRowB, vi + kPW < nkb);
+    dma_rows(xr, xslot((vi + kPX) % kNX) + wave_off, vo, (uint32_t)(vi + kPX) * kRowB, vi + kPX < nkb);
+  }
 
-  u32x4 rw[kLoads], rx[kLoads];
-  auto gload = [&](int kb) {
-    const uint32_t ko = (uint32_t)kb * kRowB;
+  // ---- shifted bias b' = b + (1 - min b) >= 1, so every selection key is a positive float ----
+  float mn = fminf(fminf(bq[0], bq[1]), fminf(bq[2], bq[3]));
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) rw[i] = load16(wr, goff + i * gstep + ko);
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) rx[i] = load16(xr, goff + i * gstep + ko);
-  };
-  auto swrite = [&](int buf) {
-    unsigned char* base = smem + buf * kStage + soff;
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) *reinterpret_cast<u32x4*>(base + i * sstep) = rw[i];
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) *reinterpret_cast<u32x4*>(base + kWBytes + i * sstep) = rx[i];
-  };
+  for (int off = 32; off > 0; off >>= 1) mn = fminf(mn, __shfl_xor(mn, off));
+  const float shift = 1.0f - mn;  // identical in every wave: min is exact
+  const float bv = tid < n_experts ? bias[tid] : 0.0f;
 
-  // Operand read offsets: row r = l32 (+32 per block), chunk 2s + h of the row segment.
-  uint32_t fo[4];
+  // Operand reads: row r = l32 (+32 per block), chunk 2s + h of the 128-byte row segment.
+  uint32_t fo[kKSteps];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) fo[s] = (uint32_t)l32 * kRowB + (uint32_t)((((2 * s + h) ^ (l32 & 7))) << 4);
-  const uint32_t xo = kWBytes + (uint32_t)wave * (kTokWave * kRowB);
+  for (int s = 0; s < kKSteps; ++s) fo[s] = (uint32_t)l32 * kRowB + (uint32_t)(swz(l32, 2 * s + h) << 4);
+  const uint32_t xo = (uint32_t)wave * (kTokWave * kRowB);
 
   f32x16 acc[kMB][kNB];
 #pragma unroll
@@ -158,39 +194,83 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
 
-  const int nkb = d / kBK;
-  gload(0);
-  swrite(0);
-  if (nkb > 1) gload(1);
-  lds_barrier();
-  for (int kb = 0; kb < nkb; ++kb) {
-    const unsigned char* sb = smem + (kb & 1) * kStage;
+  // nkb >= 1 always (d >= kBK): a do-while tells the compiler so, and spares it a second,
+  // never-run copy of the 256 zero accumulators held across the loop.
+  int j0 = 0;
+  do {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8 a[kMB], b[kNB];
-#pragma unroll
-      for (int mb = 0; mb < kMB; ++mb) a[mb] = *reinterpret_cast<const bf16x8*>(sb + fo[s] + mb * (32 * kRowB));
-#pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) b[nb] = *reinterpret_cast<const bf16x8*>(sb + xo + fo[s] + nb * (32 * kRowB));
-#pragma unroll
-      for (int mb = 0; mb < kMB; ++mb)
+    for (int u = 0; u < kUnroll; ++u) {
+      const int j = j0 + u;
+      if (j >= nkb) break;
+      // Own DMAs of stage j are done; after the barrier everyone's are, and every wave has
+      // finished reading stage j - 1, whose slots the DMAs below overwrite.
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(kVmBudget) & ~(15 << 8));  // and lgkmcnt(0)
+      bare_barrier();
+      // Weight DMAs at the head of the stage (they must precede this stage's token DMAs for
+      // the vmcnt budget); the token DMAs are spread over the MFMA stream below, so that a
+      // DMA waiting for room in the vector memory pipeline only delays MFMAs already queued.
+      dma_rows(wr, wslot((u + kPW) % kNW) + wave_off, vo, (uint32_t)(j + kPW) * kRowB, j + kPW < nkb);
+      __builtin_amdgcn_sched_barrier(0);
+      dma_rows(xr, xslot((u + kPX) % kNX) + wave_off, vo, (uint32_t)(j + kPX) * kRowB, j + kPX < nkb);
+      const unsigned char* ws = wslot(u % kNW);
+      const unsigned char* xsb = xslot(u % kNX) + xo;
+      // Operand fragments are double-buffered: the 10 LDS reads of k-step s + 1 go out before
+      // the 16 MFMAs of k-step s, so their latency hides behind 512 MFMA cycles (one wave per
+      // SIMD has no other wave to hide it).
+      bf16x8 a[2][kMB], b[2][kNB];
+      auto fetch = [&](int buf, int s) {
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
+          b[buf][nb] = *reinterpret_cast<const bf16x8*>(xsb + fo[s] + nb * (32 * kRowB));
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb)
+          a[buf][mb] = *reinterpret_cast<const bf16x8*>(ws + fo[s] + mb * (32 * kRowB));
+      };
+      fetch(0, 0);
+      fetch(1, 1);
+#pragma unroll
+      for (int s = 0; s < kKSteps; ++s) {
+        if (s >= 1 && s + 1 < kKSteps) fetch((s + 1) & 1, s + 1);
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < kNB; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][mb], b[s & 1][nb], acc[mb][nb], 0, 0, 0);
+      }
+      // Issue order for the scheduler: reads of steps 0 and 1; then per step its MFMAs with
+      // kDma / kKSteps token DMAs slotted between them, and the reads of step s + 2.
+      static_assert(kDma % kKSteps == 0 && (kMB * kNB) % (kDma / kKSteps) == 0, "DMA interleave");
+      constexpr int kDmaPerStep = kDma / kKSteps;
+      constexpr int kMfmaPerDma = kMB * kNB / kDmaPerStep;
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (kMB + kNB), 0);  // DS reads, steps 0 and 1
+#pragma unroll
+      for (int s = 0; s < kKSteps; ++s) {
+#pragma unroll
+        for (int q = 0; q < kDmaPerStep; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerDma, 0);  // MFMAs, step s
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);            // one token DMA
+        }
+        if (s + 2 < kKSteps) __builtin_amdgcn_sched_group_barrier(0x100, kMB + kNB, 0);  // DS reads, step s + 2
+      }
     }
-    if (kb + 1 < nkb) {
-      swrite((kb + 1) & 1);
-      if (kb + 2 < nkb) gload(kb + 2);
-    }
-    lds_barrier();
-  }
+    j0 += kUnroll;
+  } while (j0 < nkb);
 
   // ---- epilogue ----
-  // Output layout of a 32x32 MFMA block (rows = experts, columns = tokens): lane column
-  // l32 is the token; accumulator r holds expert row 8 (r / 4) + 4 h + (r % 4).
-  // The stage buffers are free now (every wave passed the last barrier); each wave parks
-  // its scores in its own 32 KiB slice: [32 row groups][64 lanes][4 floats].
-  float* sbuf = reinterpret_cast<float*>(smem + wave * 32768);
+  // Drain the trailing dummy DMAs (they write the slots reused below) and let every wave
+  // finish its last operand reads; then slot ws1 holds b' and the load histogram, and each
+  // wave parks its scores in a slot of its own: [32 row groups][64 lanes][4 floats].
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0) & ~(15 << 8));
+  bare_barrier();
+  float* const bprime = reinterpret_cast<float*>(ws1);
+  int* const hist = reinterpret_cast<int*>(ws1 + 1024);
+  bprime[tid] = tid < n_experts ? bv + shift : 0.0f;
+  hist[tid] = 0;
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  bare_barrier();
+  float* const park = reinterpret_cast<float*>(wave == 0 ? xs0 : wave == 1 ? xs1 : wave == 2 ? xs2 : ws0);
+  // Output layout of a 32x32 MFMA block (rows = experts, columns = tokens): lane column l32 is
+  // the token; accumulator r holds expert row 8 (r / 4) + 4 h + (r % 4).
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
     const int64_t t = row0 + wave * kTokWave + nb * 32 + l32;
@@ -208,13 +288,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         for (int r = 0; r < 4; ++r) {
           const float s = sigmoid_fast(acc[mb][nb][g * 4 + r]);
           sv[r] = s;
-          const uint32_t bits = (__float_as_uint(s + bp[r]) & 0xFFFFFF00u) | (uint32_t)(255 - (e0 + r));
-          topk_insert<K>(top, e0 + r < n_experts ? __uint_as_float(bits) : 0.0f);
+          const uint32_t slot_id = (uint32_t)(127 - (mb * 16 + g * 4 + r));  // lane-local, ascending expert
+          const float key = __uint_as_float((__float_as_uint(s + bp[r]) & 0xFFFFFF00u) | slot_id);
+          topk_insert<K>(top, FULL || e0 + r < n_experts ? key : 0.0f);
         }
-        *reinterpret_cast<f32x4*>(sbuf + ((mb * 4 + g) * 64 + lane) * 4) = sv;
+        *reinterpret_cast<f32x4*>(park + ((mb * 4 + g) * 64 + lane) * 4) = sv;
       }
     }
-    // Merge with lane ^ 32, which holds the other 128 experts of the same token.
+    // Re-key the survivors with the global expert id, then merge with lane ^ 32, which holds
+    // the other 128 experts of the same token.
+    int e[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const uint32_t bits = __float_as_uint(top[j]);
+      const int ls = 127 - (int)(bits & 0x7Fu);
+      e[j] = ((ls >> 2) << 3) | (h << 2) | (ls & 3);
+      top[j] = __uint_as_float((bits & 0xFFFFFF00u) | (uint32_t)(255 - e[j]));
+    }
     float other[K];
 #pragma unroll
     for (int j = 0; j < K; ++j) other[j] = __shfl_xor(top[j], 32);
@@ -223,14 +313,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     wave_lds_sync();
 
     if (t < T) {
-      int e[K];
       float sg[K];
       float ssum = 0.0f;
 #pragma unroll
       for (int j = 0; j < K; ++j) {
         e[j] = 255 - (int)(__float_as_uint(top[j]) & 0xFFu);
         const int src_lane = l32 + 32 * ((e[j] >> 2) & 1);
-        sg[j] = sbuf[((e[j] >> 3) * 64 + src_lane) * 4 + (e[j] & 3)];
+        sg[j] = park[((e[j] >> 3) * 64 + src_lane) * 4 + (e[j] & 3)];
         ssum += sg[j];
       }
       if (h == 0) {
@@ -259,8 +348,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int e = mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (e < n_experts) logits[t * n_experts + e] = acc[mb][nb][r];
+            const int ee = mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (ee < n_experts) logits[t * n_experts + ee] = acc[mb][nb][r];
           }
       }
       if (lse != nullptr) {
@@ -269,48 +358,55 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int e = mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (e < n_experts) m = fmaxf(m, acc[mb][nb][r]);
+            const int ee = mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (ee < n_experts) m = fmaxf(m, acc[mb][nb][r]);
           }
         float sum = 0.0f;
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int e = mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (e < n_experts) sum += __builtin_amdgcn_exp2f((acc[mb][nb][r] - m) * kLog2e);
+            const int ee = mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (ee < n_experts) sum += __builtin_amdgcn_exp2f((acc[mb][nb][r] - m) * kLog2e);
           }
         const float m2 = __shfl_xor(m, 32);
         const float sum2 = __shfl_xor(sum, 32);
         const float mm = fmaxf(m, m2);
-        const float tot = sum * __builtin_amdgcn_exp2f((m - mm) * kLog2e) + sum2 * __builtin_amdgcn_exp2f((m2 - mm) * kLog2e);
+        const float tot =
+            sum * __builtin_amdgcn_exp2f((m - mm) * kLog2e) + sum2 * __builtin_amdgcn_exp2f((m2 - mm) * kLog2e);
         if (h == 0 && t < T) lse[t] = mm + __logf(tot);
       }
     }
   }
 
-  lds_barrier();
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  bare_barrier();
   if (tid < n_experts && hist[tid] != 0) atomicAdd(&counts[tid], hist[tid]);
+}
+
+template <int K, bool FULL>
+hipError_t launch_kf(const RouterArgs& a, hipStream_t stream) {
+  const int normalize = (a.flags & ELB_GATES_RAW) ? 0 : 1;
+  const dim3 grid((unsigned)((a.T + kTile - 1) / kTile));
+  if (a.logits != nullptr || a.lse != nullptr)
+    return launch(router_mfma_kernel<K, FULL, true>, grid, dim3(kThreads), 0, stream, (const uint16_t*)a.x,
+                  (const uint16_t*)a.w, a.bias, a.T, a.d, a.n_experts, normalize, a.idx, a.gates, a.counts,
+                  a.logits, a.lse);
+  return launch(router_mfma_kernel<K, FULL, false>, grid, dim3(kThreads), 0, stream, (const uint16_t*)a.x,
+                (const uint16_t*)a.w, a.bias, a.T, a.d, a.n_experts, normalize, a.idx, a.gates, a.counts,
+                a.logits, a.lse);
 }
 
 template <int K>
 hipError_t launch_k(const RouterArgs& a, hipStream_t stream) {
-  const int normalize = (a.flags & ELB_GATES_RAW) ? 0 : 1;
-  const dim3 grid((unsigned)((a.T + kTile - 1) / kTile));
-  if (a.logits != nullptr || a.lse != nullptr)
-    return launch(router_mfma_kernel<K, true>, grid, dim3(kThreads), 0, stream, (const uint16_t*)a.x,
-                  (const uint16_t*)a.w, a.bias, a.T, a.d, a.n_experts, normalize, a.idx, a.gates, a.counts,
-                  a.logits, a.lse);
-  return launch(router_mfma_kernel<K, false>, grid, dim3(kThreads), 0, stream, (const uint16_t*)a.x,
-                (const uint16_t*)a.w, a.bias, a.T, a.d, a.n_experts, normalize, a.idx, a.gates, a.counts,
-                a.logits, a.lse);
+  return a.n_experts == kExp ? launch_kf<K, true>(a, stream) : launch_kf<K, false>(a, stream);
 }
 
 }  // namespace
 
 bool router_mfma_applies(const RouterArgs& a) {
   return a.dtype == ELB_BF16 && a.d % kBK == 0 && a.n_experts <= kExp && a.k >= 1 && a.k <= 8 &&
-         (int64_t)a.d * 2 * kExp < (1ll << 31);
+         (int64_t)a.d * 2 * kTile < (int64_t(1) << 30);
 }
 
 hipError_t launch_router_mfma(const RouterArgs& a, hipStream_t stream) {

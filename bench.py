@@ -58,6 +58,42 @@ def traffic_from_profile(T: int) -> float | None:
     return float(rec["traffic_bytes_per_launch"])
 
 
+def summarize_traffic(fetch_csv: str, write_csv: str, copy_mib: int, T: int) -> dict:
+    """HBM bytes per router launch from two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE).
+
+    Both counters report KiB per dispatch, summed here over the counter's instances.  Each is
+    scaled by what it reads for the plain device-to-device copy of known size that
+    ``--calibrate-copy`` runs in the same program (the copy reads and writes copy_mib MiB).
+    """
+    import csv
+    from collections import defaultdict
+
+    def per_kernel(path, counter, key, last=None):
+        acc = defaultdict(float)
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter and key in r["Kernel_Name"]:
+                    acc[int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+        ids = sorted(acc)[-last:] if last else sorted(acc)
+        return sum(acc[i] for i in ids) / len(ids)
+
+    # The calibration copies are the last three blits of the program (earlier blits are the
+    # host-to-device uploads of the inputs).
+    copy_bytes = copy_mib * 1024 * 1024
+    f_router = per_kernel(fetch_csv, "FETCH_SIZE", "router_mfma_kernel")
+    w_router = per_kernel(write_csv, "WRITE_SIZE", "router_mfma_kernel")
+    f_copy = per_kernel(fetch_csv, "FETCH_SIZE", "copyBuffer", last=3)
+    w_copy = per_kernel(write_csv, "WRITE_SIZE", "copyBuffer", last=3)
+    f_scale, w_scale = copy_bytes / (f_copy * 1024), copy_bytes / (w_copy * 1024)
+    return {
+        "kernel_source_sha256": kernel_source_hash(), "T": T,
+        "fetch_kib_per_launch": f_router, "write_kib_per_launch": w_router,
+        "copy_mib": copy_mib, "copy_fetch_kib": f_copy, "copy_write_kib": w_copy,
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "traffic_bytes_per_launch": f_router * 1024 * f_scale + w_router * 1024 * w_scale,
+    }
+
+
 def cpu_baseline(wl, x, w, b, m, min_seconds: float = 10.0, max_seconds: float = 30.0) -> dict:
     """The oracle (untuned) on the whole step of the same workload, repeated for >= min_seconds."""
     import numpy as np
@@ -93,7 +129,20 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="large")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="also run a device-to-device copy of MIB MiB (the byte-counter reference)")
+    ap.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_MIB"),
+                    help="write the HBM traffic record from two rocprofv3 counter runs and exit")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        import datagen
+
+        rec = summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1], int(args.summarize_traffic[2]),
+                                datagen.WORKLOADS[args.workload].T)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec))
+        return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
               file=sys.stderr)
@@ -212,6 +261,14 @@ def main() -> int:
                          "balance": round(balance_ms * 1e3, 2), "step": round(ms * 1e3, 2)},
         "maxvio_last": float(mv.cpu()[0]),
     }
+    if args.calibrate_copy:
+        n = args.calibrate_copy * 1024 * 1024
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)  # a device-to-device blit of known size
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(wl, x, w, b0, m0)
     print(json.dumps(line), flush=True)

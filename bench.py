@@ -1,8 +1,8 @@
 """Benchmark: routed tokens/s of the full router step on one MI355X.
 
 One step = router forward (logits, sigmoid, biased Top-4, gates, expert loads) + dispatch
-permutation (for workloads that dispatch) + SMEBU bias update with MaxVio, all on one stream,
-inputs resident in HBM.  Default workload: one GPU's micro-batch share of the Large-style
+permutation + SMEBU bias update with MaxVio: one elb_route_step call (three kernels) on one
+stream, inputs resident in HBM.  Default workload: one GPU's micro-batch share of the Large-style
 step, T = 65536 tokens, d = 3072, N_r = 256, K = 4, 32 Zipf clusters (synthetic).
 
     python bench.py [--steps K] [--warmup W] [--workload large] [--no-cpu]
@@ -16,7 +16,6 @@ and the CPU oracle timed on the host on the same workload.
 from __future__ import annotations
 
 import argparse
-import ctypes
 import hashlib
 import json
 import os
@@ -108,8 +107,7 @@ def cpu_baseline(wl, x, w, b, m, min_seconds: float = 10.0, max_seconds: float =
             r = oracle.route(x, w, b, wl.k)
             n = oracle.expert_loads(r.idx, wl.n_experts)
             oracle.max_violation(n)
-            if wl.dispatch:
-                oracle.dispatch_permutation(r.idx, wl.n_experts)
+            oracle.dispatch_permutation(r.idx, wl.n_experts)
             oracle.balance_step(n, b, m, mode=wl.mode, lam=wl.lam, beta=wl.beta, kappa=wl.kappa, gamma=wl.gamma)
             reps += 1
             el = time.perf_counter() - t0
@@ -117,7 +115,7 @@ def cpu_baseline(wl, x, w, b, m, min_seconds: float = 10.0, max_seconds: float =
                 break
     return {"value": reps * wl.T / el, "unit": "routed tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"the full step of {wl.label} (route + loads + MaxVio"
-                      f"{' + dispatch' if wl.dispatch else ''} + {wl.mode} update), {reps} repetition(s), "
+                      f" + dispatch + {wl.mode} update), {reps} repetition(s), "
                       f"fp64 numpy, BLAS threads={cores}",
             "seconds": round(el, 2)}
 
@@ -153,10 +151,9 @@ def main() -> int:
 
     import datagen
     import expert_load_balancing_amd as elb
-    from expert_load_balancing_amd import _lib
 
     wl = datagen.WORKLOADS[args.workload]
-    lib = elb.lib()
+    elb.lib()  # fails loudly when libelb.so is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -174,62 +171,36 @@ def main() -> int:
     xs = [to_dev(x), to_dev(x)]
     wd, bd, md = to_dev(w), to_dev(b0), to_dev(m0)
     T, d, n_e, k = wl.T, wl.d, wl.n_experts, wl.k
-    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
-    gates = torch.empty((T, k), dtype=torch.float32, device=dev)
-    counts = torch.empty(n_e, dtype=torch.int32, device=dev)
-    offsets = torch.empty(n_e + 1, dtype=torch.int32, device=dev)
-    perm = torch.empty(T * k, dtype=torch.int32, device=dev)
-    inv = torch.empty(T * k, dtype=torch.int32, device=dev)
-    ws = torch.empty(max(16, elb.dispatch_workspace_bytes(T, k, n_e)), dtype=torch.uint8, device=dev)
-    mv = torch.empty(2, dtype=torch.float32, device=dev)
-    dtype_code = elb.ELB_BF16 if wl.dtype == "bf16" else elb.ELB_F32
-    params = _lib.BalanceParams(elb.MODES[wl.mode], wl.lam, wl.beta, wl.kappa, wl.gamma)
+    # One library call per step (elb_route_step): router kernel, dispatch scan with the bias
+    # update beside it, scatter.  The loads accumulate into counts and the update clears them.
+    step = elb.RouterStep(wd, bd, md, k, T, mode=wl.mode, lam=wl.lam, beta=wl.beta, kappa=wl.kappa, gamma=wl.gamma)
     stream = torch.cuda.current_stream(dev)
-    sp = ctypes.c_void_p(stream.cuda_stream)
-    P = ctypes.c_void_p
-    xp = [P(t.data_ptr()) for t in xs]
-    wp, bp, mp = P(wd.data_ptr()), P(bd.data_ptr()), P(md.data_ptr())
-    ip, gp, cp = P(idx.data_ptr()), P(gates.data_ptr()), P(counts.data_ptr())
-    op, pp, vp, wsp, mvp = P(offsets.data_ptr()), P(perm.data_ptr()), P(inv.data_ptr()), P(ws.data_ptr()), P(mv.data_ptr())
-    ws_bytes = ws.numel()
-    null = P(0)
 
-    n_ev = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_ev)]
-
-    def step(i: int, timed: bool) -> None:
-        e = ev[i] if timed else None
-        # counts <- 0 (library fill kernel; a T = 0 forward only clears the loads)
-        _lib.check("clear", lib.elb_router_forward(null, dtype_code, 0, d, wp, bp, n_e, k, 0, null, null, cp,
-                                                   null, null, sp))
-        if e:
-            e[0].record(stream)
-        _lib.check("router", lib.elb_router_forward(xp[i & 1], dtype_code, T, d, wp, bp, n_e, k,
-                                                    elb.ELB_ACCUMULATE_COUNTS, ip, gp, cp, null, null, sp))
-        if e:
-            e[1].record(stream)
-        if wl.dispatch:
-            _lib.check("dispatch", lib.elb_router_dispatch(ip, T, k, n_e, wsp, ws_bytes, op, pp, vp, sp))
-        if e:
-            e[2].record(stream)
-        _lib.check("balance", lib.elb_smebu_update(cp, n_e, params, bp, mp, null, mvp, sp))
-        if e:
-            e[3].record(stream)
+    # Per timed step: events around the router kernel (recorded by the library on its stream)
+    # and one after the step.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e in ev:
+        for one in e:
+            one.record(stream)  # creates the HIP event before the timed region
+    torch.cuda.synchronize()
 
     for i in range(args.warmup):
-        step(i, False)
+        step(xs[i & 1])
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for i in range(args.steps):
-        step(i, True)
+        e = ev[i]
+        step.set_timing(e[0], e[1])
+        out = step(xs[i & 1])
+        e[2].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
     router_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    dispatch_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    balance_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    rest_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     value = T / (ms * 1e-3)
+    mv = out.maxvio
 
     alg = router_alg_bytes(T, d, n_e, k)
     achieved = alg / (router_ms * 1e-3) / 1e9
@@ -250,15 +221,15 @@ def main() -> int:
         "dtype": "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": wl.label, "T": T, "d": d, "n_experts": n_e, "k": k, "balance": wl.mode,
-                   "dispatch": wl.dispatch, "parallelism": "none (1 GPU)"},
+                   "dispatch": True, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else round(traffic),
                      "kernel": "router_mfma_kernel<4>", "alg_bytes_per_launch": alg,
                      "kernel_us": round(router_ms * 1e3, 2),
                      "mfma_tflops": round(tflops, 1), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)},
-        "breakdown_us": {"router": round(router_ms * 1e3, 2), "dispatch": round(dispatch_ms * 1e3, 2),
-                         "balance": round(balance_ms * 1e3, 2), "step": round(ms * 1e3, 2)},
+        "breakdown_us": {"router": round(router_ms * 1e3, 2), "dispatch+update": round(rest_ms * 1e3, 2),
+                         "step": round(ms * 1e3, 2)},
         "maxvio_last": float(mv.cpu()[0]),
     }
     if args.calibrate_copy:

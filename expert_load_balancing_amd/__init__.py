@@ -8,17 +8,25 @@ kernels on the current torch stream.  Nothing here computes the method itself.
     idx, gates, counts = router_forward(x, w, bias, k=4)
     offsets, perm, inv = router_dispatch(idx, n_experts=256)
     delta_b, maxvio = smebu_update(counts, bias, momentum)      # updates bias, momentum in place
+
+or, for a training loop with one batch per optimizer step, all three in three kernels with
+buffers allocated once:
+
+    step = RouterStep(w, bias, momentum, k=4, max_tokens=T)
+    out = step(x)            # out.topk_idx, out.gates, out.offsets, out.perm, out.maxvio, ...
 """
 
 from __future__ import annotations
 
 import ctypes
+from typing import NamedTuple
 
 import torch
 
 from ._lib import (  # noqa: F401
     ELB_ACCUMULATE_COUNTS,
     ELB_BF16,
+    ELB_CLEAR_COUNTS,
     ELB_F32,
     ELB_FORCE_GENERIC,
     ELB_GATES_RAW,
@@ -27,12 +35,13 @@ from ._lib import (  # noqa: F401
     ELB_MODE_SMEBU,
     BalanceParams,
     ElbError,
+    StepArgs,
     check,
     lib,
 )
 
 __all__ = ["router_forward", "router_dispatch", "dispatch_workspace_bytes", "smebu_update", "maxvio",
-           "version", "ElbError", "MODES"]
+           "RouterStep", "StepOutputs", "version", "ElbError", "MODES"]
 
 MODES = {"smebu": ELB_MODE_SMEBU, "sign": ELB_MODE_SIGN, "linear": ELB_MODE_LINEAR}
 _DTYPES = {torch.float32: ELB_F32, torch.bfloat16: ELB_BF16}
@@ -138,8 +147,11 @@ def router_dispatch(topk_idx: torch.Tensor, n_experts: int, *, workspace: torch.
 
 def smebu_update(counts: torch.Tensor, bias: torch.Tensor, momentum: torch.Tensor | None, *, mode: str = "smebu",
                  lam: float = 5e-4, beta: float = 0.5, kappa: float = 2.0, gamma: float = 1e-3,
-                 want_delta: bool = False, want_maxvio: bool = True):
-    """Update bias (and momentum) in place from one step's counts.  Returns (delta_b or None, maxvio[2] or None)."""
+                 want_delta: bool = False, want_maxvio: bool = True, clear_counts: bool = False):
+    """Update bias (and momentum) in place from one step's counts.  Returns (delta_b or None, maxvio[2] or None).
+
+    With ``clear_counts`` the counts are zeroed once read, ready for the next step's accumulation.
+    """
     _need(counts, "counts", torch.int32)
     dev = counts.device
     _need(bias, "bias", torch.float32, dev)
@@ -152,7 +164,7 @@ def smebu_update(counts: torch.Tensor, bias: torch.Tensor, momentum: torch.Tenso
         raise ValueError(f"mode must be one of {sorted(MODES)}")
     delta = torch.empty(n_e, dtype=torch.float32, device=dev) if want_delta else None
     mv = torch.empty(2, dtype=torch.float32, device=dev) if want_maxvio else None
-    params = BalanceParams(MODES[mode], lam, beta, kappa, gamma)
+    params = BalanceParams(MODES[mode], lam, beta, kappa, gamma, ELB_CLEAR_COUNTS if clear_counts else 0)
     st = lib().elb_smebu_update(_ptr(counts), n_e, params, _ptr(bias), _ptr(momentum), _ptr(delta), _ptr(mv),
                                 _stream(dev))
     check("elb_smebu_update", st)
@@ -165,3 +177,99 @@ def maxvio(counts: torch.Tensor) -> torch.Tensor:
     out = torch.empty(2, dtype=torch.float32, device=counts.device)
     check("elb_maxvio", lib().elb_maxvio(_ptr(counts), counts.numel(), _ptr(out), _stream(counts.device)))
     return out
+
+
+class StepOutputs(NamedTuple):
+    """Views of one RouterStep call's outputs (valid until the next call)."""
+
+    topk_idx: torch.Tensor   # [T, k] int32
+    gates: torch.Tensor      # [T, k] fp32
+    counts: torch.Tensor     # [N_r] int32 (zero after a step that cleared them)
+    offsets: torch.Tensor    # [N_r + 1] int32
+    perm: torch.Tensor       # [T * k] int32
+    inv_perm: torch.Tensor | None
+    lse: torch.Tensor | None
+    delta_b: torch.Tensor | None
+    maxvio: torch.Tensor | None
+
+
+class RouterStep:
+    """Route, dispatch and (optionally) update the expert bias in one library call (elb_route_step).
+
+    Holds the router weight w [N_r, d], the bias b [N_r] and momentum m [N_r] (updated in place
+    when ``update``), and output buffers sized for up to ``max_tokens`` tokens, allocated once.
+    ``counts`` start at zero; with ``update`` and ``clear_counts`` each call routes with the
+    current bias, then applies one bias update from this batch's loads and leaves the counts
+    zeroed for the next call.  Without ``update`` the loads accumulate across calls (several
+    micro-batches per optimizer step) until an update with ``clear_counts`` consumes them.
+    """
+
+    def __init__(self, w: torch.Tensor, bias: torch.Tensor, momentum: torch.Tensor | None, k: int, max_tokens: int,
+                 *, update: bool = True, mode: str = "smebu", lam: float = 5e-4, beta: float = 0.5,
+                 kappa: float = 2.0, gamma: float = 1e-3, clear_counts: bool = True, gates_raw: bool = False,
+                 want_inv: bool = True, want_lse: bool = False, want_delta: bool = False, want_maxvio: bool = True,
+                 force_generic: bool = False):
+        _need(w, "w")
+        dev = w.device
+        if w.dtype not in _DTYPES:
+            raise TypeError(f"w must be float32 or bfloat16, got {w.dtype}")
+        _need(bias, "bias", torch.float32, dev)
+        if momentum is not None:
+            _need(momentum, "momentum", torch.float32, dev)
+        n_e, d = w.shape
+        if bias.shape != (n_e,) or (momentum is not None and momentum.shape != (n_e,)):
+            raise ValueError("bias and momentum must have one entry per row of w")
+        if mode not in MODES:
+            raise ValueError(f"mode must be one of {sorted(MODES)}")
+        self.w, self.bias, self.momentum, self.k, self.max_tokens = w, bias, momentum, k, max_tokens
+        self.device = dev
+        T, i32, f32 = max_tokens, torch.int32, torch.float32
+        self.topk_idx = torch.empty((T, k), dtype=i32, device=dev)
+        self.gates = torch.empty((T, k), dtype=f32, device=dev)
+        self.counts = torch.zeros(n_e, dtype=i32, device=dev)
+        self.offsets = torch.empty(n_e + 1, dtype=i32, device=dev)
+        self.perm = torch.empty(T * k, dtype=i32, device=dev)
+        self.inv_perm = torch.empty(T * k, dtype=i32, device=dev) if want_inv else None
+        self.lse = torch.empty(T, dtype=f32, device=dev) if want_lse else None
+        self.delta_b = torch.empty(n_e, dtype=f32, device=dev) if (update and want_delta) else None
+        self.maxvio = torch.empty(2, dtype=f32, device=dev) if (update and want_maxvio) else None
+        ws_bytes = dispatch_workspace_bytes(T, k, n_e)
+        self.workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        flags = ELB_ACCUMULATE_COUNTS | (ELB_GATES_RAW if gates_raw else 0) | (ELB_FORCE_GENERIC if force_generic else 0)
+        a = StepArgs()
+        a.dtype, a.d, a.w, a.bias = _DTYPES[w.dtype], d, w.data_ptr(), bias.data_ptr()
+        a.n_experts, a.k, a.flags = n_e, k, flags
+        a.topk_idx, a.gates, a.counts = self.topk_idx.data_ptr(), self.gates.data_ptr(), self.counts.data_ptr()
+        a.logits, a.lse = None, _ptr(self.lse).value
+        a.workspace, a.workspace_bytes = self.workspace.data_ptr(), self.workspace.numel()
+        a.offsets, a.perm, a.inv_perm = self.offsets.data_ptr(), self.perm.data_ptr(), _ptr(self.inv_perm).value
+        a.update = 1 if update else 0
+        a.params = BalanceParams(MODES[mode], lam, beta, kappa, gamma, ELB_CLEAR_COUNTS if clear_counts else 0)
+        a.momentum, a.delta_b, a.maxvio = _ptr(momentum).value, _ptr(self.delta_b).value, _ptr(self.maxvio).value
+        a.timing = None
+        self._args = a
+        self._timing = None
+
+    def set_timing(self, start: torch.cuda.Event | None, stop: torch.cuda.Event | None = None) -> None:
+        """Record ``start``/``stop`` (timing-enabled torch events) around the router kernel of later calls."""
+        if start is None:
+            self._timing, self._args.timing = None, None
+            return
+        for ev in (start, stop):
+            if ev.cuda_event == 0:  # torch creates the HIP event on first record
+                ev.record(torch.cuda.current_stream(self.device))
+        self._timing = (ctypes.c_void_p * 2)(start.cuda_event, stop.cuda_event)
+        self._args.timing = ctypes.cast(self._timing, ctypes.c_void_p).value
+
+    def __call__(self, x: torch.Tensor) -> StepOutputs:
+        _need(x, "x", self.w.dtype, self.device)
+        T = x.shape[0]
+        if x.dim() != 2 or x.shape[1] != self.w.shape[1] or T > self.max_tokens:
+            raise ValueError(f"x must be [T <= {self.max_tokens}, {self.w.shape[1]}], got {tuple(x.shape)}")
+        a = self._args
+        a.x, a.T = x.data_ptr(), T
+        check("elb_route_step", lib().elb_route_step(ctypes.byref(a), _stream(self.device)))
+        k = self.k
+        return StepOutputs(self.topk_idx[:T], self.gates[:T], self.counts, self.offsets, self.perm[:T * k],
+                           None if self.inv_perm is None else self.inv_perm[:T * k],
+                           None if self.lse is None else self.lse[:T], self.delta_b, self.maxvio)

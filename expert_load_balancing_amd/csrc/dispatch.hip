@@ -3,29 +3,37 @@
 // The pages define no dispatch; what is computed is the plain stable counting sort:
 // bucket e holds the flat positions routed to expert e in ascending order, offsets[e] is
 // the bucket start, and inv is the inverse permutation.  Positions come from an
-// expert-major, tile-ordered exclusive scan of per-tile histograms plus a stable rank
-// inside the tile, never from the order in which atomics happen to land, so the result is
+// expert-major, tile-ordered exclusive scan of per-tile loads plus a stable rank inside the
+// tile, never from the order in which atomics happen to land, so the result is
 // bit-identical run to run.
 //
-//  1. hist:     one workgroup per tile of E entries (E chosen so there are at most 256
-//               tiles): LDS histogram -> ws[e][tile].
-//  2. tilescan: one wave per expert: ws[e][tile] <- sum of hist[e][tile'] for tile' < tile,
-//               and the expert's total.
-//  3. scatter:  one workgroup per tile.  Each block scans the 256 expert totals itself (a few
-//               hundred cycles) to get the bucket starts, then walks its tile in chunks of
-//               256 entries in flat order: a wave finds the lanes that hold the same expert
-//               with 8 ballots (one per bit of e) and ranks them by lane; waves of a chunk are
-//               ranked through LDS counters.
-// Workspace: ws [n_experts][n_tiles] int32, then totals [n_experts] int32.
+// A tile is 256 tokens, all K slots of each: 256 K consecutive flat entries.  Workspace:
+//   loads  [n_experts][stride] int32: entries of tile b routed to expert e, then (after the
+//          scan) the number of such entries in tiles before b;
+//   totals [n_experts] int32.
+//  1. loads:   one workgroup per tile, LDS histogram.  Skipped when the MFMA router kernel
+//              already stored its own tile histogram in the table.
+//  2. scan:    one wave per expert scans its row in place and writes the expert's total.  With
+//              a bias update requested, one more workgroup runs it (balance_wave.hpp): the
+//              update reads only `counts`, which are final once the router kernel is done.
+//  3. scatter: one workgroup per tile, one pass.  Each block scans the expert totals itself
+//              (a few hundred cycles) for the bucket starts.  Entry c * 256 + tid of the tile
+//              goes to thread tid; each 64-entry run ("virtual wave" v = c * 4 + wave, in
+//              ascending j) ranks its lanes by expert with 8 ballots (one per bit of e), the
+//              last lane of each expert stores the run's count, and one in-place scan per
+//              expert over the runs turns those counts into run offsets.
+#include "balance_wave.hpp"
 #include "device_common.hpp"
 #include "elb_kernels.h"
 
 namespace elb {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = kDispatchTile;  // one thread per token (per entry of a chunk)
+constexpr int kWaves = kThreads / 64;
 constexpr int kMaxExperts = 256;
-constexpr int kMaxTiles = 256;
+
+using i32x4 = int __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
   const int lane = threadIdx.x & 63;
@@ -37,146 +45,186 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v;
 }
 
-__global__ __launch_bounds__(kThreads) void dispatch_hist_kernel(const int32_t* __restrict__ idx, int64_t total,
-                                                                 int64_t tile_entries, int n_experts, int n_tiles,
-                                                                 int32_t* __restrict__ ws) {
+__global__ __launch_bounds__(kThreads) void dispatch_loads_kernel(const int32_t* __restrict__ idx, int64_t total,
+                                                                  int k, int n_experts, int64_t stride,
+                                                                  int32_t* __restrict__ loads) {
   __shared__ int hist[kMaxExperts];
   hist[threadIdx.x] = 0;
   __syncthreads();
-  const int64_t lo = (int64_t)blockIdx.x * tile_entries;
-  const int64_t hi = lo + tile_entries < total ? lo + tile_entries : total;
+  const int64_t lo = (int64_t)blockIdx.x * kDispatchTile * k;
+  const int64_t hi = lo + (int64_t)kDispatchTile * k < total ? lo + (int64_t)kDispatchTile * k : total;
   for (int64_t j = lo + threadIdx.x; j < hi; j += kThreads) {
     const int e = idx[j];
     if ((unsigned)e < (unsigned)n_experts) atomicAdd(&hist[e], 1);  // out-of-range ids are dropped
   }
   __syncthreads();
-  if ((int)threadIdx.x < n_experts) ws[(int64_t)threadIdx.x * n_tiles + blockIdx.x] = hist[threadIdx.x];
+  if ((int)threadIdx.x < n_experts) loads[(int64_t)threadIdx.x * stride + blockIdx.x] = hist[threadIdx.x];
 }
 
-__global__ __launch_bounds__(64) void dispatch_tilescan_kernel(int32_t* __restrict__ ws, int n_tiles,
-                                                               int32_t* __restrict__ totals) {
-  const int e = blockIdx.x;
-  const int lane = threadIdx.x;
-  int32_t* row = ws + (int64_t)e * n_tiles;
-  int v[kMaxTiles / 64];
-#pragma unroll
-  for (int c = 0; c < kMaxTiles / 64; ++c) {
-    const int t = c * 64 + lane;
-    v[c] = t < n_tiles ? row[t] : 0;
+// Blocks 0 .. n_experts-1: scan one row each.  Block n_experts (launched only with an update):
+// the bias update.
+__global__ __launch_bounds__(64) void dispatch_scan_kernel(int32_t* __restrict__ loads, int64_t n_tiles,
+                                                           int64_t stride, int n_experts,
+                                                           int32_t* __restrict__ totals, BalanceArgs update) {
+  if ((int)blockIdx.x == n_experts) {
+    balance_wave(update);
+    return;
   }
+  const int lane = threadIdx.x;
+  int32_t* const row = loads + (int64_t)blockIdx.x * stride;
   int carry = 0;
+  for (int64_t c0 = 0; c0 < n_tiles; c0 += 256) {
+    const int64_t t0 = c0 + 4 * lane;  // stride % 4 == 0: t0 < stride covers t0 .. t0 + 3
+    i32x4 v = {0, 0, 0, 0};
+    if (t0 < stride) v = *reinterpret_cast<const i32x4*>(row + t0);
 #pragma unroll
-  for (int c = 0; c < kMaxTiles / 64; ++c) {
-    const int t = c * 64 + lane;
-    const int incl = wave_inclusive_scan(v[c]);
-    if (t < n_tiles) row[t] = carry + incl - v[c];
+    for (int q = 0; q < 4; ++q)
+      if (t0 + q >= n_tiles) v[q] = 0;  // padding columns hold stale workspace
+    const int local = v[0] + v[1] + v[2] + v[3];
+    const int incl = wave_inclusive_scan(local);
+    const int excl = carry + incl - local;
+    if (t0 < stride)
+      *reinterpret_cast<i32x4*>(row + t0) = i32x4{excl, excl + v[0], excl + v[0] + v[1], excl + v[0] + v[1] + v[2]};
     carry += __shfl(incl, 63);
   }
-  if (lane == 0) totals[e] = carry;
+  if (lane == 0) totals[blockIdx.x] = carry;
 }
 
+template <int K>
 __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(const int32_t* __restrict__ idx, int64_t total,
-                                                                    int64_t tile_entries, int n_experts, int n_tiles,
-                                                                    const int32_t* __restrict__ ws,
+                                                                    int n_experts, int64_t stride,
+                                                                    const int32_t* __restrict__ loads,
                                                                     const int32_t* __restrict__ totals,
                                                                     int32_t* __restrict__ offsets,
                                                                     int32_t* __restrict__ perm,
                                                                     int32_t* __restrict__ inv) {
-  __shared__ int base[kMaxExperts];
-  __shared__ int wave_sum[kThreads / 64];
-  __shared__ int wave_cnt[kThreads / 64][kMaxExperts];
+  __shared__ int wsum[kWaves];
+  __shared__ int vcnt[K * kWaves][kMaxExperts];  // per virtual wave: count, then start
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int64_t lo = (int64_t)blockIdx.x * (kDispatchTile * K);
 
-  // Bucket starts: exclusive scan of the expert totals, then this tile's own offset.
-  const int tot = tid < n_experts ? totals[tid] : 0;
-  const int incl = wave_inclusive_scan(tot);
-  if (lane == 63) wave_sum[wave] = incl;
+  int e[K];
 #pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) wave_cnt[w][tid] = 0;
+  for (int c = 0; c < K; ++c) {
+    const int64_t j = lo + c * kThreads + tid;
+    const int raw = j < total ? idx[j] : -1;
+    e[c] = (unsigned)raw < (unsigned)n_experts ? raw : -1;  // out-of-range ids are dropped
+  }
+  const int tot = tid < n_experts ? totals[tid] : 0;
+  const int before = tid < n_experts ? loads[(int64_t)tid * stride + blockIdx.x] : 0;
+#pragma unroll
+  for (int v = 0; v < K * kWaves; ++v) vcnt[v][tid] = 0;
+
+  // Bucket start of expert tid: exclusive scan of the totals.
+  const int incl = wave_inclusive_scan(tot);
+  if (lane == 63) wsum[wave] = incl;
   __syncthreads();
   int start = incl - tot;
-  for (int w = 0; w < wave; ++w) start += wave_sum[w];
-  if (tid < n_experts) {
-    base[tid] = start + ws[(int64_t)tid * n_tiles + blockIdx.x];
-    if (blockIdx.x == 0) offsets[tid] = start;
+  for (int w = 0; w < wave; ++w) start += wsum[w];
+  if (blockIdx.x == 0) {
+    if (tid < n_experts) offsets[tid] = start;
+    if (tid == 0) offsets[n_experts] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
   }
-  if (blockIdx.x == 0 && tid == 0) {
-    int all = 0;
-    for (int w = 0; w < kThreads / 64; ++w) all += wave_sum[w];
-    offsets[n_experts] = all;
-  }
-  __syncthreads();
 
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int64_t lo = (int64_t)blockIdx.x * tile_entries;
-  const int64_t hi = lo + tile_entries < total ? lo + tile_entries : total;
-  for (int64_t c0 = lo; c0 < hi; c0 += kThreads) {
-    const int64_t j = c0 + tid;
-    const int raw = j < hi ? idx[j] : -1;
-    const bool valid = (unsigned)raw < (unsigned)n_experts;  // out-of-range ids are dropped
-    const int e = valid ? raw : 0;
+  // Rank inside each 64-entry run: lanes below with the same expert.
+  const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  int rank[K];
+#pragma unroll
+  for (int c = 0; c < K; ++c) {
+    const bool valid = e[c] >= 0;
+    const int key = valid ? e[c] : 0;
     uint64_t peers = __ballot(valid);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-      const uint64_t m = __ballot((e >> b) & 1);
-      peers &= ((e >> b) & 1) ? m : ~m;
+      const uint64_t m = __ballot((key >> b) & 1);
+      peers &= ((key >> b) & 1) ? m : ~m;
     }
-    const int rank = __popcll(peers & lt_mask);
+    rank[c] = __popcll(peers & lt_mask);
     const int cnt = __popcll(peers);
-    if (valid && rank == cnt - 1) wave_cnt[wave][e] = cnt;  // the last peer in lane order
-    __syncthreads();
-    if (valid) {
-      int pos = base[e] + rank;
-      for (int w = 0; w < wave; ++w) pos += wave_cnt[w][e];
+    if (valid && rank[c] == cnt - 1) vcnt[c * kWaves + wave][key] = cnt;  // the last peer in lane order
+  }
+  __syncthreads();
+  // Run offsets of expert tid: its bucket start, plus earlier tiles, plus earlier runs.
+  if (tid < n_experts) {
+    int run = start + before;
+#pragma unroll
+    for (int v = 0; v < K * kWaves; ++v) {
+      const int x = vcnt[v][tid];
+      vcnt[v][tid] = run;
+      run += x;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < K; ++c) {
+    if (e[c] >= 0) {
+      const int64_t j = lo + c * kThreads + tid;
+      const int pos = vcnt[c * kWaves + wave][e[c]] + rank[c];
       perm[pos] = (int32_t)j;
       if (inv != nullptr) inv[j] = pos;
     }
-    __syncthreads();
-    if (tid < n_experts) {
-      int add = 0;
-#pragma unroll
-      for (int w = 0; w < kThreads / 64; ++w) {
-        add += wave_cnt[w][tid];
-        wave_cnt[w][tid] = 0;
-      }
-      base[tid] += add;
-    }
-    __syncthreads();
   }
+}
+
+template <int K>
+hipError_t launch_scatter(const int32_t* idx, int64_t total, int n_experts, const DispatchGeom& g,
+                          const int32_t* loads, const int32_t* totals, int32_t* offsets, int32_t* perm, int32_t* inv,
+                          hipStream_t stream) {
+  return launch(dispatch_scatter_kernel<K>, dim3((unsigned)g.n_tiles), dim3(kThreads), 0, stream, idx, total,
+                n_experts, g.stride, loads, totals, offsets, perm, inv);
 }
 
 }  // namespace
 
-int64_t dispatch_tile_entries(int64_t total) {
-  // At most kMaxTiles tiles, never fewer than 1024 entries per tile.
-  int64_t t = 1024;
-  while (t * kMaxTiles < total) t <<= 1;
-  return t;
+DispatchGeom dispatch_geometry(int64_t T) {
+  DispatchGeom g;
+  g.n_tiles = (T + kDispatchTile - 1) / kDispatchTile;
+  g.stride = (g.n_tiles + 3) / 4 * 4;
+  return g;
 }
 
-size_t dispatch_workspace_bytes(int64_t total, int n_experts) {
-  if (total <= 0) return 0;
-  const int64_t te = dispatch_tile_entries(total);
-  const int64_t n_tiles = (total + te - 1) / te;
-  return (size_t)(n_tiles * n_experts + n_experts) * sizeof(int32_t);
+size_t dispatch_workspace_bytes(int64_t T, int n_experts) {
+  if (T <= 0) return 0;
+  const DispatchGeom g = dispatch_geometry(T);
+  return (size_t)(g.stride * n_experts + n_experts) * sizeof(int32_t);
 }
 
-hipError_t launch_dispatch(const int32_t* idx, int64_t total, int n_experts, void* workspace, int32_t* offsets,
-                           int32_t* perm, int32_t* inv, hipStream_t stream) {
-  if (total == 0) return launch_fill_i32(offsets, n_experts + 1, 0, stream);
-  const int64_t te = dispatch_tile_entries(total);
-  const int n_tiles = (int)((total + te - 1) / te);
-  int32_t* ws = static_cast<int32_t*>(workspace);
-  int32_t* totals = ws + (int64_t)n_tiles * n_experts;
-  hipError_t err = launch(dispatch_hist_kernel, dim3(n_tiles), dim3(kThreads), 0, stream, idx, total, te,
-                          n_experts, n_tiles, ws);
+hipError_t launch_dispatch(const int32_t* idx, int64_t T, int k, int n_experts, void* workspace, bool loads_ready,
+                           const BalanceArgs* update, int32_t* offsets, int32_t* perm, int32_t* inv,
+                           hipStream_t stream) {
+  if (T == 0) {
+    const hipError_t err = launch_fill_i32(offsets, n_experts + 1, 0, stream);
+    if (err != hipSuccess || update == nullptr) return err;
+    return launch_balance(*update, stream);
+  }
+  const DispatchGeom g = dispatch_geometry(T);
+  const int64_t total = T * k;
+  int32_t* loads = static_cast<int32_t*>(workspace);
+  int32_t* totals = loads + g.stride * n_experts;
+  hipError_t err = hipSuccess;
+  if (!loads_ready) {
+    err = launch(dispatch_loads_kernel, dim3((unsigned)g.n_tiles), dim3(kThreads), 0, stream, idx, total, k,
+                 n_experts, g.stride, loads);
+    if (err != hipSuccess) return err;
+  }
+  const BalanceArgs none{};
+  err = launch(dispatch_scan_kernel, dim3((unsigned)(n_experts + (update != nullptr ? 1 : 0))), dim3(64), 0, stream,
+               loads, g.n_tiles, g.stride, n_experts, totals, update != nullptr ? *update : none);
   if (err != hipSuccess) return err;
-  err = launch(dispatch_tilescan_kernel, dim3(n_experts), dim3(64), 0, stream, ws, n_tiles, totals);
-  if (err != hipSuccess) return err;
-  return launch(dispatch_scatter_kernel, dim3(n_tiles), dim3(kThreads), 0, stream, idx, total, te, n_experts,
-                n_tiles, (const int32_t*)ws, (const int32_t*)totals, offsets, perm, inv);
+  const int32_t* cl = loads;
+  const int32_t* ct = totals;
+  switch (k) {
+    case 1: return launch_scatter<1>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, stream);
+    case 2: return launch_scatter<2>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, stream);
+    case 3: return launch_scatter<3>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, stream);
+    case 4: return launch_scatter<4>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, stream);
+    case 5: return launch_scatter<5>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, stream);
+    case 6: return launch_scatter<6>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, stream);
+    case 7: return launch_scatter<7>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, stream);
+    default: return launch_scatter<8>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, stream);
+  }
 }
 
 }  // namespace elb

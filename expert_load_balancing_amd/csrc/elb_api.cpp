@@ -1,5 +1,5 @@
 // C-ABI entry points of libelb: argument checks, then kernel selection and launch.
-// Every check happens before anything is queued; see include/elb.h for the contract.
+// Every check happens before anything is queued; include/elb.h states the contract.
 #include "../../include/elb.h"
 
 #include "elb_kernels.h"
@@ -11,14 +11,11 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 elb_status from_hip(hipError_t e) { return e == hipSuccess ? ELB_OK : ELB_ERR_LAUNCH; }
 
 constexpr uint32_t kKnownFlags = ELB_GATES_RAW | ELB_ACCUMULATE_COUNTS | ELB_FORCE_GENERIC;
+constexpr uint32_t kKnownBalanceFlags = ELB_CLEAR_COUNTS;
 
-}  // namespace
-
-extern "C" {
-
-elb_status elb_router_forward(const void* x, int32_t dtype, int64_t T, int32_t d, const void* w, const float* bias,
-                              int32_t n_experts, int32_t k, uint32_t flags, int32_t* topk_idx, float* gates,
-                              int32_t* counts, float* logits, float* lse, elb_stream_t stream) {
+elb_status check_forward(const void* x, int32_t dtype, int64_t T, int32_t d, const void* w, const float* bias,
+                         int32_t n_experts, int32_t k, uint32_t flags, const int32_t* topk_idx, const float* gates,
+                         const int32_t* counts, const float* logits, const float* lse) {
   if (w == nullptr || bias == nullptr || counts == nullptr) return ELB_ERR_NULL;
   if (T > 0 && (x == nullptr || topk_idx == nullptr || gates == nullptr)) return ELB_ERR_NULL;
   if (dtype != ELB_F32 && dtype != ELB_BF16) return ELB_ERR_UNSUPPORTED;
@@ -29,14 +26,60 @@ elb_status elb_router_forward(const void* x, int32_t dtype, int64_t T, int32_t d
   if ((d * elem) % 16 != 0 || !aligned(w, 16)) return ELB_ERR_ALIGN;
   if (T > 0 && (!aligned(x, 16) || !aligned(topk_idx, 16) || !aligned(gates, 16))) return ELB_ERR_ALIGN;
   if (!aligned(bias, 4) || !aligned(counts, 4) || !aligned(logits, 4) || !aligned(lse, 4)) return ELB_ERR_ALIGN;
+  return ELB_OK;
+}
 
+elb_status check_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t n_experts, const void* workspace,
+                          size_t workspace_bytes, const int32_t* offsets, const int32_t* perm,
+                          const int32_t* inv_perm) {
+  if (offsets == nullptr) return ELB_ERR_NULL;
+  if (T > 0 && (topk_idx == nullptr || perm == nullptr || workspace == nullptr)) return ELB_ERR_NULL;
+  if (T < 0 || k < 1 || k > 8 || n_experts < 1 || n_experts > 256) return ELB_ERR_SHAPE;
+  if (T * (int64_t)k >= (int64_t(1) << 31)) return ELB_ERR_SHAPE;
+  if (workspace_bytes < elb::dispatch_workspace_bytes(T, n_experts)) return ELB_ERR_WORKSPACE;
+  if (!aligned(topk_idx, 4) || !aligned(offsets, 4) || !aligned(perm, 4) || !aligned(inv_perm, 4) ||
+      !aligned(workspace, 16))
+    return ELB_ERR_ALIGN;
+  return ELB_OK;
+}
+
+elb_status check_update(const int32_t* counts, int32_t n_experts, const elb_balance_params& params, const float* bias,
+                        const float* momentum, const float* delta_b, const float* maxvio) {
+  if (params.mode != ELB_MODE_SMEBU && params.mode != ELB_MODE_SIGN && params.mode != ELB_MODE_LINEAR)
+    return ELB_ERR_UNSUPPORTED;
+  if (params.flags & ~kKnownBalanceFlags) return ELB_ERR_UNSUPPORTED;
+  if (counts == nullptr || bias == nullptr) return ELB_ERR_NULL;
+  if (params.mode != ELB_MODE_SIGN && momentum == nullptr) return ELB_ERR_NULL;
+  if (n_experts < 1 || n_experts > 1024) return ELB_ERR_SHAPE;
+  if (!aligned(counts, 4) || !aligned(bias, 4) || !aligned(momentum, 4) || !aligned(delta_b, 4) || !aligned(maxvio, 4))
+    return ELB_ERR_ALIGN;
+  return ELB_OK;
+}
+
+elb::BalanceArgs balance_args(int32_t* counts, int32_t n_experts, const elb_balance_params& p, float* bias,
+                              float* momentum, float* delta_b, float* maxvio) {
+  return elb::BalanceArgs{counts, n_experts, p.mode, p.lambda, p.beta, p.kappa, p.gamma,
+                          (p.flags & ELB_CLEAR_COUNTS) ? 1 : 0, bias, momentum, delta_b, maxvio};
+}
+
+}  // namespace
+
+extern "C" {
+
+elb_status elb_router_forward(const void* x, int32_t dtype, int64_t T, int32_t d, const void* w, const float* bias,
+                              int32_t n_experts, int32_t k, uint32_t flags, int32_t* topk_idx, float* gates,
+                              int32_t* counts, float* logits, float* lse, elb_stream_t stream) {
+  const elb_status st =
+      check_forward(x, dtype, T, d, w, bias, n_experts, k, flags, topk_idx, gates, counts, logits, lse);
+  if (st != ELB_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (!(flags & ELB_ACCUMULATE_COUNTS)) {
     const hipError_t err = elb::launch_fill_i32(counts, n_experts, 0, s);
     if (err != hipSuccess) return ELB_ERR_LAUNCH;
   }
   if (T == 0) return ELB_OK;
-  const elb::RouterArgs a{x, dtype, T, d, w, bias, n_experts, k, flags, topk_idx, gates, counts, logits, lse};
+  const elb::RouterArgs a{x,      dtype, T,      d,   w,   bias,    n_experts, k,
+                          flags,  topk_idx, gates, counts, logits, lse, nullptr, 0};
   if (!(flags & ELB_FORCE_GENERIC) && elb::router_mfma_applies(a)) return from_hip(elb::launch_router_mfma(a, s));
   return from_hip(elb::launch_router_generic(a, s));
 }
@@ -44,36 +87,64 @@ elb_status elb_router_forward(const void* x, int32_t dtype, int64_t T, int32_t d
 size_t elb_dispatch_workspace_bytes(int64_t T, int32_t k, int32_t n_experts) {
   if (T < 0 || k < 1 || k > 8 || n_experts < 1 || n_experts > 256) return 0;
   if (T * (int64_t)k >= (int64_t(1) << 31)) return 0;
-  return elb::dispatch_workspace_bytes(T * (int64_t)k, n_experts);
+  return elb::dispatch_workspace_bytes(T, n_experts);
 }
 
 elb_status elb_router_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t n_experts, void* workspace,
                                size_t workspace_bytes, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
                                elb_stream_t stream) {
-  if (offsets == nullptr) return ELB_ERR_NULL;
-  if (T > 0 && (topk_idx == nullptr || perm == nullptr || workspace == nullptr)) return ELB_ERR_NULL;
-  if (T < 0 || k < 1 || k > 8 || n_experts < 1 || n_experts > 256) return ELB_ERR_SHAPE;
-  if (T * (int64_t)k >= (int64_t(1) << 31)) return ELB_ERR_SHAPE;
-  if (workspace_bytes < elb::dispatch_workspace_bytes(T * (int64_t)k, n_experts)) return ELB_ERR_WORKSPACE;
-  if (!aligned(topk_idx, 4) || !aligned(offsets, 4) || !aligned(perm, 4) || !aligned(inv_perm, 4) ||
-      !aligned(workspace, 16))
-    return ELB_ERR_ALIGN;
+  const elb_status st =
+      check_dispatch(topk_idx, T, k, n_experts, workspace, workspace_bytes, offsets, perm, inv_perm);
+  if (st != ELB_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  return from_hip(elb::launch_dispatch(topk_idx, T * (int64_t)k, n_experts, workspace, offsets, perm, inv_perm, s));
+  return from_hip(elb::launch_dispatch(topk_idx, T, k, n_experts, workspace, false, nullptr, offsets, perm, inv_perm, s));
 }
 
-elb_status elb_smebu_update(const int32_t* counts, int32_t n_experts, elb_balance_params params, float* bias,
+elb_status elb_smebu_update(int32_t* counts, int32_t n_experts, elb_balance_params params, float* bias,
                             float* momentum, float* delta_b, float* maxvio, elb_stream_t stream) {
-  if (params.mode != ELB_MODE_SMEBU && params.mode != ELB_MODE_SIGN && params.mode != ELB_MODE_LINEAR)
-    return ELB_ERR_UNSUPPORTED;
-  if (counts == nullptr || bias == nullptr) return ELB_ERR_NULL;
-  if (params.mode != ELB_MODE_SIGN && momentum == nullptr) return ELB_ERR_NULL;
-  if (n_experts < 1 || n_experts > 1024) return ELB_ERR_SHAPE;
-  if (!aligned(counts, 4) || !aligned(bias, 4) || !aligned(momentum, 4) || !aligned(delta_b, 4) || !aligned(maxvio, 4))
-    return ELB_ERR_ALIGN;
+  const elb_status st = check_update(counts, n_experts, params, bias, momentum, delta_b, maxvio);
+  if (st != ELB_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  return from_hip(elb::launch_balance(counts, n_experts, params.mode, params.lambda, params.beta, params.kappa,
-                                      params.gamma, bias, momentum, delta_b, maxvio, s));
+  return from_hip(elb::launch_balance(balance_args(counts, n_experts, params, bias, momentum, delta_b, maxvio), s));
+}
+
+elb_status elb_route_step(const elb_step_args* args, elb_stream_t stream) {
+  if (args == nullptr) return ELB_ERR_NULL;
+  const elb_step_args& a = *args;
+  elb_status st = check_forward(a.x, a.dtype, a.T, a.d, a.w, a.bias, a.n_experts, a.k, a.flags, a.topk_idx, a.gates,
+                                a.counts, a.logits, a.lse);
+  if (st != ELB_OK) return st;
+  st = check_dispatch(a.topk_idx, a.T, a.k, a.n_experts, a.workspace, a.workspace_bytes, a.offsets, a.perm,
+                      a.inv_perm);
+  if (st != ELB_OK) return st;
+  if (a.update != 0) {
+    st = check_update(a.counts, a.n_experts, a.params, a.bias, a.momentum, a.delta_b, a.maxvio);
+    if (st != ELB_OK) return st;
+  }
+  if (a.timing != nullptr && (a.timing[0] == nullptr || a.timing[1] == nullptr)) return ELB_ERR_NULL;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (!(a.flags & ELB_ACCUMULATE_COUNTS)) {
+    if (elb::launch_fill_i32(a.counts, a.n_experts, 0, s) != hipSuccess) return ELB_ERR_LAUNCH;
+  }
+  const elb::DispatchGeom g = elb::dispatch_geometry(a.T);
+  elb::RouterArgs ra{a.x,     a.dtype,    a.T,      a.d,      a.w,     a.bias, a.n_experts,
+                     a.k,     a.flags,    a.topk_idx, a.gates, a.counts, a.logits, a.lse,
+                     static_cast<int32_t*>(a.workspace), g.stride};
+  const bool mfma = !(a.flags & ELB_FORCE_GENERIC) && elb::router_mfma_applies(ra);
+  if (!mfma) ra.tile_loads = nullptr;
+  if (a.timing != nullptr && hipEventRecord(static_cast<hipEvent_t>(a.timing[0]), s) != hipSuccess)
+    return ELB_ERR_LAUNCH;
+  if (a.T > 0) {
+    const hipError_t err = mfma ? elb::launch_router_mfma(ra, s) : elb::launch_router_generic(ra, s);
+    if (err != hipSuccess) return ELB_ERR_LAUNCH;
+  }
+  if (a.timing != nullptr && hipEventRecord(static_cast<hipEvent_t>(a.timing[1]), s) != hipSuccess)
+    return ELB_ERR_LAUNCH;
+  const elb::BalanceArgs upd =
+      balance_args(a.counts, a.n_experts, a.params, a.bias, a.momentum, a.delta_b, a.maxvio);
+  return from_hip(elb::launch_dispatch(a.topk_idx, a.T, a.k, a.n_experts, a.workspace, mfma,
+                                       a.update != 0 ? &upd : nullptr, a.offsets, a.perm, a.inv_perm, s));
 }
 
 elb_status elb_maxvio(const int32_t* counts, int32_t n_experts, float* out, elb_stream_t stream) {
@@ -81,7 +152,9 @@ elb_status elb_maxvio(const int32_t* counts, int32_t n_experts, float* out, elb_
   if (n_experts < 1 || n_experts > 1024) return ELB_ERR_SHAPE;
   if (!aligned(counts, 4) || !aligned(out, 4)) return ELB_ERR_ALIGN;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  return from_hip(elb::launch_balance(counts, n_experts, -1, 0.f, 0.f, 0.f, 0.f, nullptr, nullptr, nullptr, out, s));
+  const elb::BalanceArgs a{const_cast<int32_t*>(counts), n_experts, -1, 0.f, 0.f, 0.f, 0.f, 0,
+                           nullptr, nullptr, nullptr, out};
+  return from_hip(elb::launch_balance(a, s));
 }
 
 const char* elb_status_str(elb_status status) {

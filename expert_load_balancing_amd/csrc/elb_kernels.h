@@ -26,6 +26,21 @@ struct RouterArgs {
   int32_t* counts;
   float* logits;
   float* lse;
+  int32_t* tile_loads;   // NULL, or the dispatch workspace's [n_experts][loads_stride] table:
+  int64_t loads_stride;  // the MFMA kernel then stores each 256-token tile's loads in it
+};
+
+// One bias update / MaxVio (balance_wave.hpp).  mode < 0: MaxVio only.
+struct BalanceArgs {
+  int32_t* counts;
+  int n;
+  int mode;
+  float lambda, beta, kappa, gamma;
+  int clear;  // zero `counts` once read
+  float* bias;
+  float* momentum;
+  float* delta_b;
+  float* maxvio;
 };
 
 // Launch `kernel` and return the runtime's verdict instead of dropping it.
@@ -47,14 +62,21 @@ bool router_mfma_applies(const RouterArgs& a);
 hipError_t launch_router_mfma(const RouterArgs& a, hipStream_t stream);
 hipError_t launch_router_generic(const RouterArgs& a, hipStream_t stream);
 
-int64_t dispatch_tile_entries(int64_t total);
-size_t dispatch_workspace_bytes(int64_t total, int n_experts);
-hipError_t launch_dispatch(const int32_t* idx, int64_t total, int n_experts, void* workspace,
-                           int32_t* offsets, int32_t* perm, int32_t* inv, hipStream_t stream);
+// Dispatch works on tiles of kDispatchTile tokens (all K slots of each): the MFMA router's own
+// tile, so that kernel can hand over its per-tile loads.
+constexpr int kDispatchTile = 256;
+struct DispatchGeom {
+  int64_t n_tiles;  // ceil(T / kDispatchTile)
+  int64_t stride;   // row stride of the loads table: n_tiles rounded up to a multiple of 4
+};
+DispatchGeom dispatch_geometry(int64_t T);
+size_t dispatch_workspace_bytes(int64_t T, int n_experts);
+// loads_ready: the router kernel already filled the loads table for this batch.
+// update: NULL, or a bias update to run beside the scan (one extra workgroup).
+hipError_t launch_dispatch(const int32_t* idx, int64_t T, int k, int n_experts, void* workspace, bool loads_ready,
+                           const BalanceArgs* update, int32_t* offsets, int32_t* perm, int32_t* inv,
+                           hipStream_t stream);
 
-// mode < 0: MaxVio only (no update).
-hipError_t launch_balance(const int32_t* counts, int n_experts, int mode, float lambda, float beta,
-                          float kappa, float gamma, float* bias, float* momentum, float* delta_b,
-                          float* maxvio, hipStream_t stream);
+hipError_t launch_balance(const BalanceArgs& a, hipStream_t stream);
 
 }  // namespace elb

@@ -74,7 +74,6 @@ constexpr int kKSteps = kBK / 16;         // MFMA k-steps per stage
 static_assert(kNX + kNW <= 8, "at most 8 DMA target slots");
 static_assert((kNX + kNW) * kSlot <= 160 * 1024, "LDS");
 constexpr int kDma = kSlot / (kWaves * 1024);  // DMA instructions per wave per slot (1 KiB each)
-constexpr uint32_t kOOB = 0x7FFFFF00u;    // voffset outside every buffer: dummy DMA
 constexpr float kLog2e = 1.4426950408889634f;
 
 static_assert(kNX == kPX + 1 && kNW == kPW + 1 && kUnroll % kNX == 0 && kUnroll % kNW == 0, "ring shape");
@@ -99,12 +98,27 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 #define ELB_AS3(p) ((__attribute__((address_space(3))) void*)(p))
 
-// One wave's share of one slot: kDma 1-KiB DMA instructions (8 rows each).
-__device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, unsigned char* wave_base, const uint32_t (&vo)[kDma],
-                                         uint32_t soff, bool real) {
+// Cache policy of the DMAs: the token rows are read exactly once, so they go non-temporal
+// (nt): streaming them through the caches with normal allocation costs the L2-resident router
+// weights their place and the whole memory pipeline ~20% of its rate.
+constexpr int kAuxTokens = 2;   // nt
+constexpr int kAuxWeights = 0;  // default: keep the weights cached
+
+// One wave's share of one slot: kDma 1-KiB DMA instructions (8 rows each).  A dummy DMA (past
+// the last stage) keeps the vmcnt budget uniform: it goes through `none`, a descriptor with an
+// empty range, so it reads zeros and moves no bytes.  The choice is a scalar select of the
+// descriptor; the row offsets stay in their own registers.  (Selecting the offset per DMA
+// instead put a VALU write to one shared register before every DMA, which stalls behind the
+// previous DMA's operand read whenever the vector memory queue is full, and with it every
+// MFMA queued behind.)
+template <int AUX>
+__device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, __amdgpu_buffer_rsrc_t none,
+                                         unsigned char* wave_base, const uint32_t (&vo)[kDma], uint32_t soff,
+                                         bool real) {
+  const __amdgpu_buffer_rsrc_t use = real ? r : none;
 #pragma unroll
   for (int i = 0; i < kDma; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, ELB_AS3(wave_base + i * 1024), 16, real ? vo[i] : kOOB, (int)soff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(use, ELB_AS3(wave_base + i * 1024), 16, vo[i], (int)soff, 0, AUX);
 }
 
 // LDS position of 16-byte chunk c of a 128-byte row segment r.  The LDS serves 16 lanes x 16
@@ -129,7 +143,8 @@ template <int K, bool FULL, bool EXTRA>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void router_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const float* __restrict__ bias, int64_t T, int d,
     int n_experts, int normalize, int32_t* __restrict__ idx_out, float* __restrict__ gates_out,
-    int32_t* __restrict__ counts, float* __restrict__ logits, float* __restrict__ lse) {
+    int32_t* __restrict__ counts, float* __restrict__ logits, float* __restrict__ lse,
+    int32_t* __restrict__ tile_loads, int64_t loads_stride) {
   // The five ring slots are the whole LDS; the epilogue reuses them once the ring drains.
   __shared__ __attribute__((aligned(1024))) unsigned char xs0[kSlot], xs1[kSlot], xs2[kSlot];
   __shared__ __attribute__((aligned(1024))) unsigned char ws0[kSlot], ws1[kSlot];
@@ -155,6 +170,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const uint32_t row_bytes = (uint32_t)d * 2u;
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + row0 * d, (uint32_t)rows * row_bytes);
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, (uint32_t)n_experts * row_bytes);
+  const __amdgpu_buffer_rsrc_t none = make_rsrc(w, 0u);
   // DMA lane mapping: instruction i of wave `wave` fills rows wave*64 + 8 i + lane/8; lane
   // position p = lane & 7 in the row receives the global chunk stored there, swz(row, p)
   // (the swizzle is its own inverse).
@@ -169,8 +185,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // order the steady state uses (weights first, then tokens, per virtual iteration).
 #pragma unroll
   for (int vi = -kPX; vi < 0; ++vi) {
-    if (vi + kPW >= 0) dma_rows(wr, wslot((vi + kPW) % kNW) + wave_off, vo, (uint32_t)(vi + kPW) * kRowB, vi + kPW < nkb);
-    dma_rows(xr, xslot((vi + kPX) % kNX) + wave_off, vo, (uint32_t)(vi + kPX) * kRowB, vi + kPX < nkb);
+    if (vi + kPW >= 0) dma_rows<kAuxWeights>(wr, none, wslot((vi + kPW) % kNW) + wave_off, vo, (uint32_t)(vi + kPW) * kRowB, vi + kPW < nkb);
+    dma_rows<kAuxTokens>(xr, none, xslot((vi + kPX) % kNX) + wave_off, vo, (uint32_t)(vi + kPX) * kRowB, vi + kPX < nkb);
   }
 
   // ---- shifted bias b' = b + (1 - min b) >= 1, so every selection key is a positive float ----
@@ -209,9 +225,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       // Weight DMAs at the head of the stage (they must precede this stage's token DMAs for
       // the vmcnt budget); the token DMAs are spread over the MFMA stream below, so that a
       // DMA waiting for room in the vector memory pipeline only delays MFMAs already queued.
-      dma_rows(wr, wslot((u + kPW) % kNW) + wave_off, vo, (uint32_t)(j + kPW) * kRowB, j + kPW < nkb);
+      dma_rows<kAuxWeights>(wr, none, wslot((u + kPW) % kNW) + wave_off, vo, (uint32_t)(j + kPW) * kRowB, j + kPW < nkb);
       __builtin_amdgcn_sched_barrier(0);
-      dma_rows(xr, xslot((u + kPX) % kNX) + wave_off, vo, (uint32_t)(j + kPX) * kRowB, j + kPX < nkb);
+      dma_rows<kAuxTokens>(xr, none, xslot((u + kPX) % kNX) + wave_off, vo, (uint32_t)(j + kPX) * kRowB, j + kPX < nkb);
       const unsigned char* ws = wslot(u % kNW);
       const unsigned char* xsb = xslot(u % kNX) + xo;
       // Operand fragments are double-buffered: the 10 LDS reads of k-step s + 1 go out before
@@ -381,7 +397,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   bare_barrier();
-  if (tid < n_experts && hist[tid] != 0) atomicAdd(&counts[tid], hist[tid]);
+  if (tid < n_experts) {
+    const int n = hist[tid];
+    if (n != 0) atomicAdd(&counts[tid], n);
+    // This tile's loads for the dispatch scan (the workgroup is the dispatch tile).
+    if (tile_loads != nullptr) tile_loads[(int64_t)tid * loads_stride + blockIdx.x] = n;
+  }
 }
 
 template <int K, bool FULL>
@@ -391,10 +412,10 @@ hipError_t launch_kf(const RouterArgs& a, hipStream_t stream) {
   if (a.logits != nullptr || a.lse != nullptr)
     return launch(router_mfma_kernel<K, FULL, true>, grid, dim3(kThreads), 0, stream, (const uint16_t*)a.x,
                   (const uint16_t*)a.w, a.bias, a.T, a.d, a.n_experts, normalize, a.idx, a.gates, a.counts,
-                  a.logits, a.lse);
+                  a.logits, a.lse, a.tile_loads, a.loads_stride);
   return launch(router_mfma_kernel<K, FULL, false>, grid, dim3(kThreads), 0, stream, (const uint16_t*)a.x,
                 (const uint16_t*)a.w, a.bias, a.T, a.d, a.n_experts, normalize, a.idx, a.gates, a.counts,
-                a.logits, a.lse);
+                a.logits, a.lse, a.tile_loads, a.loads_stride);
 }
 
 template <int K>
@@ -403,6 +424,8 @@ hipError_t launch_k(const RouterArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+static_assert(kTile == kDispatchTile, "the router tile must be the dispatch tile");
 
 bool router_mfma_applies(const RouterArgs& a) {
   return a.dtype == ELB_BF16 && a.d % kBK == 0 && a.n_experts <= kExp && a.k >= 1 && a.k <= 8 &&

@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define ELB_VERSION 10000 /* major * 10000 + minor * 100 + patch */
+#define ELB_VERSION 10100 /* major * 10000 + minor * 100 + patch */
 
 typedef struct ihipStream_t* elb_stream_t; /* hipStream_t; NULL = default stream */
 
@@ -64,12 +64,20 @@ enum {
                                       kernel applies (tests compare the two)                 */
 };
 
+/* Flags of elb_balance_params. */
+enum {
+  ELB_CLEAR_COUNTS = 1u << 0 /* after the update, set `counts` to zero, so the next step's
+                                elb_router_forward can add into it (ELB_ACCUMULATE_COUNTS)
+                                without a separate reset                                   */
+};
+
 typedef struct {
-  int32_t mode; /* elb_mode                                                       */
-  float lambda; /* SMEBU / linear step size (Trinity Large: 5e-4)                   */
-  float beta;   /* momentum factor (Trinity Large: 0.5)                             */
-  float kappa;  /* tanh slope (Trinity Large: 2)                                    */
-  float gamma;  /* sign-step size                                                   */
+  int32_t mode;   /* elb_mode                                                     */
+  float lambda;   /* SMEBU / linear step size (Trinity Large: 5e-4)                 */
+  float beta;     /* momentum factor (Trinity Large: 0.5)                           */
+  float kappa;    /* tanh slope (Trinity Large: 2)                                  */
+  float gamma;    /* sign-step size                                                 */
+  uint32_t flags; /* ELB_CLEAR_COUNTS or 0                                          */
 } elb_balance_params;
 
 /*
@@ -134,12 +142,61 @@ elb_status elb_router_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, in
  * SIGN:   b += gamma * sign(nbar - n); b -= mean(b).
  * LINEAR: as SMEBU with tanh(kappa * v) replaced by v.
  * When every count is 0 the step is skipped (b, m unchanged, delta_b = 0, maxvio NaN).
+ * With ELB_CLEAR_COUNTS in params.flags, `counts` is zeroed once it has been read.
  * Supported: 1 <= n_experts <= 1024.  Errors: ELB_ERR_NULL, ELB_ERR_SHAPE,
- * ELB_ERR_UNSUPPORTED (mode), ELB_ERR_LAUNCH.
+ * ELB_ERR_UNSUPPORTED (mode or flag), ELB_ERR_LAUNCH.
  */
-elb_status elb_smebu_update(const int32_t* counts, int32_t n_experts, elb_balance_params params,
+elb_status elb_smebu_update(int32_t* counts, int32_t n_experts, elb_balance_params params,
                             float* bias, float* momentum, float* delta_b, float* maxvio,
                             elb_stream_t stream);
+
+/*
+ * One routed step in three kernels: elb_router_forward, then elb_router_dispatch of its
+ * topk_idx, then (when `update` is non-zero) elb_smebu_update from `counts`.  Each field
+ * means what the argument of the same name means in those calls, and the same checks apply.
+ * Compared with the three calls in a row, the router kernel stores each 256-token tile's loads
+ * in the dispatch workspace (the dispatch does not count them again; bf16 inputs with
+ * d % 64 == 0 only, else a counting pass runs), and the bias update runs inside the dispatch's
+ * scan launch.  The update sees `counts` after this batch's loads were added, and changes
+ * `bias` only after the router kernel has read it, so the next step routes with the new bias.
+ * A training loop with one batch per optimizer step sets ELB_ACCUMULATE_COUNTS and
+ * ELB_CLEAR_COUNTS and never resets `counts` itself (they must start at zero).
+ * timing: NULL, or two hipEvent_t recorded on `stream` right before and right after the
+ * router kernel (a measuring aid; both must be valid events).
+ */
+typedef struct {
+  /* elb_router_forward */
+  const void* x;
+  int32_t dtype;
+  int64_t T;
+  int32_t d;
+  const void* w;
+  float* bias;
+  int32_t n_experts;
+  int32_t k;
+  uint32_t flags;
+  int32_t* topk_idx;
+  float* gates;
+  int32_t* counts;
+  float* logits;
+  float* lse;
+  /* elb_router_dispatch */
+  void* workspace;
+  size_t workspace_bytes;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* inv_perm;
+  /* elb_smebu_update, run when update != 0 */
+  int32_t update;
+  elb_balance_params params;
+  float* momentum;
+  float* delta_b;
+  float* maxvio;
+  /* measuring aid */
+  void* const* timing;
+} elb_step_args;
+
+elb_status elb_route_step(const elb_step_args* args, elb_stream_t stream);
 
 /*
  * MaxVio of one step's loads: out[0] = max n / min n (the talk's definition, section

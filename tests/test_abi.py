@@ -4,6 +4,7 @@ rejects bad arguments with the documented status before queueing anything."""
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -70,10 +71,13 @@ def test_empty_batch_may_pass_null_token_buffers(lib):
 
 
 def test_dispatch_workspace_size(lib):
-    # 65536 x 4 entries -> 256 tiles of 1024 entries; ws = 256 x 256 tile counts + 256 totals.
+    # Tiles of 256 tokens: a [n_experts][n_tiles rounded up to 4] table of tile loads, then
+    # the n_experts totals.
     assert lib.elb_dispatch_workspace_bytes(65536, 4, 256) == (256 * 256 + 256) * 4
-    assert lib.elb_dispatch_workspace_bytes(262144, 4, 256) == (256 * 256 + 256) * 4
-    assert lib.elb_dispatch_workspace_bytes(10, 2, 16) == (1 * 16 + 16) * 4
+    assert lib.elb_dispatch_workspace_bytes(262144, 4, 256) == (1024 * 256 + 256) * 4
+    assert lib.elb_dispatch_workspace_bytes(262144, 1, 256) == (1024 * 256 + 256) * 4
+    assert lib.elb_dispatch_workspace_bytes(10, 2, 16) == (4 * 16 + 16) * 4
+    assert lib.elb_dispatch_workspace_bytes(1300, 8, 64) == (8 * 64 + 64) * 4
     assert lib.elb_dispatch_workspace_bytes(0, 4, 256) == 0
     assert lib.elb_dispatch_workspace_bytes(-1, 4, 256) == 0
     assert lib.elb_dispatch_workspace_bytes(16, 4, 300) == 0
@@ -95,12 +99,12 @@ def test_router_dispatch_rejects(lib, kw, want):
 @pytest.mark.parametrize("kw,want", [
     (dict(mode=3), UNSUPPORTED), (dict(mode=-1), UNSUPPORTED), (dict(counts=None), NULL), (dict(bias=None), NULL),
     (dict(momentum=None), NULL), (dict(momentum=None, mode=2), NULL), (dict(n=0), SHAPE), (dict(n=1025), SHAPE),
-    (dict(bias=FAKE + 1), ALIGN),
+    (dict(bias=FAKE + 1), ALIGN), (dict(flags=2), UNSUPPORTED), (dict(flags=1 << 31), UNSUPPORTED),
 ])
 def test_smebu_update_rejects(lib, kw, want):
-    a = dict(counts=FAKE, n=256, mode=0, bias=FAKE, momentum=FAKE, delta=None, mv=None)
+    a = dict(counts=FAKE, n=256, mode=0, bias=FAKE, momentum=FAKE, delta=None, mv=None, flags=0)
     a.update(kw)
-    p = _lib.BalanceParams(a["mode"], 5e-4, 0.5, 2.0, 1e-3)
+    p = _lib.BalanceParams(a["mode"], 5e-4, 0.5, 2.0, 1e-3, a["flags"])
     assert lib.elb_smebu_update(a["counts"], a["n"], p, a["bias"], a["momentum"], a["delta"], a["mv"], None) == want
 
 
@@ -111,5 +115,63 @@ def test_maxvio_rejects(lib):
     assert lib.elb_maxvio(FAKE, 2000, FAKE, None) == SHAPE
 
 
-def test_balance_params_layout():
-    assert ctypes.sizeof(_lib.BalanceParams) == 20
+def step_args(**kw):
+    a = _lib.StepArgs()
+    base = dict(x=FAKE, dtype=1, T=4096, d=256, w=FAKE, bias=FAKE, n_experts=256, k=4, flags=2, topk_idx=FAKE,
+                gates=FAKE, counts=FAKE, logits=None, lse=None, workspace=FAKE, workspace_bytes=1 << 20,
+                offsets=FAKE, perm=FAKE, inv_perm=None, update=1, momentum=FAKE, delta_b=None, maxvio=None,
+                timing=None)
+    params = dict(mode=0, lambda_=5e-4, beta=0.5, kappa=2.0, gamma=1e-3, flags=1)
+    for key, val in kw.items():
+        (params if key.startswith("p_") else base)[key[2:] if key.startswith("p_") else key] = val
+    for key, val in base.items():
+        setattr(a, key, val)
+    a.params = _lib.BalanceParams(**params)
+    return a
+
+
+@pytest.mark.parametrize("kw,want", [
+    # forward checks
+    (dict(w=None), NULL), (dict(x=None), NULL), (dict(counts=None), NULL), (dict(dtype=5), UNSUPPORTED),
+    (dict(flags=1 << 9), UNSUPPORTED), (dict(k=9), SHAPE), (dict(n_experts=300), SHAPE), (dict(d=100), ALIGN),
+    # dispatch checks
+    (dict(offsets=None), NULL), (dict(perm=None), NULL), (dict(workspace=None), NULL),
+    (dict(workspace_bytes=64), WORKSPACE), (dict(workspace=FAKE + 4), ALIGN),
+    # update checks, only when the update is asked for
+    (dict(p_mode=7), UNSUPPORTED), (dict(p_flags=4), UNSUPPORTED), (dict(momentum=None), NULL),
+    (dict(momentum=None, p_mode=1, p_flags=0, update=1, bias=FAKE + 1), ALIGN),
+])
+def test_route_step_rejects(lib, kw, want):
+    assert lib.elb_route_step(ctypes.byref(step_args(**kw)), None) == want
+
+
+def test_route_step_null_args(lib):
+    assert lib.elb_route_step(None, None) == NULL
+
+
+def test_route_step_half_timing_pair(lib):
+    pair = (ctypes.c_void_p * 2)(FAKE, None)
+    a = step_args(timing=ctypes.cast(pair, ctypes.c_void_p).value)
+    assert lib.elb_route_step(ctypes.byref(a), None) == NULL
+
+
+def _c_layout(struct: str, fields: list[str], tmp_path) -> dict:
+    """offsetof/sizeof of a struct of include/elb.h as the host C compiler lays it out."""
+    src = tmp_path / "layout.c"
+    lines = [f'printf("{f} %zu\\n", offsetof({struct}, {f}));' for f in fields]
+    src.write_text("#include <stddef.h>\n#include <stdio.h>\n#include \"elb.h\"\nint main(void) {\n" +
+                   "\n".join(lines) + f'\nprintf("sizeof %zu\\n", sizeof({struct}));\nreturn 0;\n}}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
+    return {ln.split()[0]: int(ln.split()[1]) for ln in out.splitlines()}
+
+
+@pytest.mark.parametrize("cls,cname", [(_lib.BalanceParams, "elb_balance_params"), (_lib.StepArgs, "elb_step_args")])
+def test_struct_layout_matches_header(cls, cname, tmp_path):
+    names = [f for f, _ in cls._fields_]
+    c_names = ["lambda" if f == "lambda_" else f for f in names]
+    got = _c_layout(cname, c_names, tmp_path)
+    for f, cf in zip(names, c_names):
+        assert getattr(cls, f).offset == got[cf], (cname, cf)
+    assert ctypes.sizeof(cls) == got["sizeof"]

@@ -14,6 +14,7 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("T,k,n_e,skew", [
     (1, 1, 16, 0.0), (1, 4, 256, 0.0), (257, 4, 256, 0.0), (1000, 2, 16, 1.5), (4096, 4, 256, 1.2),
     (65536, 4, 256, 1.1), (70001, 3, 200, 0.8), (262144, 4, 256, 1.1), (5, 8, 8, 0.0),
+    (1300, 8, 64, 1.0), (513, 5, 256, 0.0), (777, 6, 100, 2.0), (2049, 7, 9, 0.0), (300, 1, 1, 0.0),
 ])
 def test_dispatch_matches_oracle(T, k, n_e, skew):
     log(f"dispatch T={T} K={k} N_r={n_e} skew={skew}")
@@ -39,6 +40,18 @@ def test_dispatch_single_expert_and_empty():
     offs, perm, inv = elb.router_dispatch(empty, 256)
     torch.cuda.synchronize()
     assert (offs.cpu().numpy() == 0).all() and perm.numel() == 0
+
+
+def test_dispatch_concentrated_and_repeated_ids():
+    # Every token picks the same experts (each 64-lane run holds one expert 64 times), and
+    # tokens that name one expert in several slots (the sort is defined for any ids).
+    same = np.tile(np.array([[3, 1, 2, 0]], dtype=np.int32), (5000, 1))
+    rng = np.random.default_rng(11)
+    rep = rng.integers(0, 3, size=(3001, 4)).astype(np.int32)
+    for idx, n_e in ((same, 256), (rep, 3), (rep, 256)):
+        offs, perm, inv = elb.router_dispatch(to_dev(idx), n_e)
+        torch.cuda.synchronize()
+        check_dispatch(offs.cpu().numpy(), perm.cpu().numpy(), inv.cpu().numpy(), idx, n_e)
 
 
 def test_dispatch_without_inverse_and_reused_workspace():
@@ -125,3 +138,21 @@ def test_maxvio_entry_point():
         mv = elb.maxvio(to_dev(arr))
         torch.cuda.synchronize()
         check_maxvio(mv.cpu().numpy(), arr)
+
+
+@pytest.mark.parametrize("mode", ["smebu", "sign"])
+def test_balance_clear_counts(mode):
+    """ELB_CLEAR_COUNTS: identical update, and the loads are zero afterwards."""
+    rng = np.random.default_rng(5)
+    c = random_counts(rng, 256, 4 * 65536, skew=2.0)
+    b0 = (rng.standard_normal(256) * 0.01).astype(np.float32)
+    m0 = (rng.standard_normal(256) * 1e-4).astype(np.float32)
+    outs = []
+    for clear in (False, True):
+        cd, bd, md = to_dev(c), to_dev(b0), to_dev(m0)
+        delta, mv = elb.smebu_update(cd, bd, md, mode=mode, want_delta=True, clear_counts=clear)
+        torch.cuda.synchronize()
+        outs.append([t.cpu().numpy() for t in (bd, md, delta, mv)])
+        assert (cd.cpu().numpy() == (0 if clear else c)).all()
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)

@@ -20,7 +20,8 @@ Parity status of every function is listed in the functions' docstrings; all are 
 by tests under tests/ (closed forms, brute force, invariants, library routines).
 """
 
-from .balance import BalanceStep, balance_step, normalized_violation  # noqa: F401
+from .backward import RouterGrads, logit_grads, router_backward, router_loss  # noqa: F401
+from .balance import BalanceStep, balance_layers, balance_step, normalized_violation  # noqa: F401
 from .loads import dispatch_permutation, expert_loads, max_violation  # noqa: F401
 from .router import (  # noqa: F401
     Route,
@@ -31,4 +32,5 @@ from .router import (  # noqa: F401
     sigmoid_scores,
     widen,
 )
-from .zloss import router_z_loss  # noqa: F401
+from .moe import combine, permute_rows  # noqa: F401
+from .zloss import router_z_loss, z_loss_from_lse  # noqa: F401

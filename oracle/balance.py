@@ -75,3 +75,10 @@ def balance_step(counts: np.ndarray, bias: np.ndarray, momentum: np.ndarray, *, 
     m_new = beta * m + (1.0 - beta) * db
     b_new = b + m_new
     return BalanceStep(b_new, m_new, db, db_raw)
+
+
+def balance_layers(counts: np.ndarray, bias: np.ndarray, momentum: np.ndarray, **params) -> list[BalanceStep]:
+    """One update per MoE layer, each from its own layer's loads: every layer carries its own
+    b and m, and no equation on the pages couples layers ("SMEBU Load Balancing", "How it
+    works": the update is stated per router).  counts, bias, momentum are [L, N_r]."""
+    return [balance_step(counts[l], bias[l], momentum[l], **params) for l in range(len(counts))]

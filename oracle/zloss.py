@@ -24,3 +24,9 @@ def router_z_loss(z: np.ndarray) -> tuple[float, np.ndarray]:
     zmax = z.max(axis=1, keepdims=True)
     lse = (zmax + np.log(np.exp(z - zmax).sum(axis=1, keepdims=True)))[:, 0]
     return float(np.mean(lse * lse)), lse
+
+
+def z_loss_from_lse(lse: np.ndarray) -> float:
+    """mean_t lse_t^2 from per-token log-sum-exps (the same reading as router_z_loss)."""
+    lse = np.asarray(lse, dtype=np.float64)
+    return float(np.mean(lse * lse)) if lse.size else 0.0

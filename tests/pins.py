@@ -393,4 +393,147 @@ def pin_zloss(orc):
     _close(loss, sum(v * v for v in want) / 4, rtol=1e-14, what="mean square")
 
 
+def pin_zloss_from_lse(orc):
+    """mean of squares of given per-token lse values, against a plain loop."""
+    lse = [1.5, -2.0, 0.25, 3.0]
+    _close(orc.z_loss_from_lse(np.array(lse)), sum(v * v for v in lse) / 4, rtol=1e-15, what="mean lse^2")
+    assert orc.z_loss_from_lse(np.zeros(0)) == 0.0
+
+
+# ------------------------------------------------------------------ layers ---------------
+
+def pin_layers_independent(orc):
+    """L layers updated at once equal L single-layer updates, and a layer's result depends only
+    on its own loads: the worked example's layer is unaffected by its neighbours."""
+    counts = np.array([[8, 4, 2, 2], [1, 1, 1, 1], [0, 0, 0, 0]])
+    b0 = np.array([[0.01, -0.02, 0.005, 0.005], [0.1, 0.2, 0.3, 0.4], [0.5, 0.5, -1.0, 0.0]])
+    m0 = np.zeros((3, 4))
+    steps = orc.balance_layers(counts, b0, m0)
+    t1, t2 = _tanh(1.0), _tanh(2.0)
+    db = [LAM * v for v in (-t2, 0.0, t1, t1)]
+    mean = sum(db) / 4
+    b1 = [b0[0][i] + (1 - BETA) * (db[i] - mean) for i in range(4)]
+    _close(steps[0].bias, b1, rtol=1e-14, what="layer 0 worked example")
+    _close(steps[1].bias, b0[1], rtol=0, what="uniform layer unchanged")
+    _close(steps[2].bias, b0[2], rtol=0, what="empty layer skipped")
+    assert len(steps) == 3
+
+
+# ------------------------------------------------------------------ permute / combine ----
+
+def pin_permute_buckets(orc):
+    """The expert-contiguous rows against a bucket loop over (token, slot) in order."""
+    rng = np.random.default_rng(31)
+    n_e, k = 7, 3
+    idx = np.stack([rng.choice(n_e, size=k, replace=False) for _ in range(40)])
+    x = rng.integers(0, 2 ** 16, size=(40, 5)).astype(np.uint16)
+    want = []
+    for e in range(n_e):
+        for t in range(40):
+            for j in range(k):
+                if idx[t, j] == e:
+                    want.append(x[t])
+    _, perm, _ = orc.dispatch_permutation(idx, n_e)
+    got = orc.permute_rows(x, perm, k)
+    assert got.dtype == np.uint16 and (got == np.array(want)).all()
+
+
+def pin_combine_direct(orc):
+    """Combine through the permutation equals sum_j g[t,j] * E_{idx[t,j]}(x_t) computed token by
+    token, for per-expert affine maps E_e(u) = (e + 1) u + e."""
+    rng = np.random.default_rng(37)
+    n_e, k, T, d = 6, 2, 25, 4
+    idx = np.stack([rng.choice(n_e, size=k, replace=False) for _ in range(T)])
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    g = rng.random((T, k))
+    _, perm, inv = orc.dispatch_permutation(idx, n_e)
+    xp = orc.permute_rows(x, perm, k).astype(np.float64)
+    e_of_row = idx.ravel()[perm]
+    eo = ((e_of_row[:, None] + 1.0) * xp + e_of_row[:, None]).astype(np.float32)
+    got = orc.combine(eo, g, inv, k)
+    for t in range(T):
+        for c in range(d):
+            want = 0.0
+            for j in range(k):
+                e = int(idx[t, j])
+                want += g[t, j] * float(np.float32((e + 1.0) * float(x[t, c]) + e))
+            assert abs(got[t, c] - want) <= 1e-12 * (1 + abs(want)), (t, c, got[t, c], want)
+
+
+def pin_combine_identity_experts(orc):
+    """Identity experts and normalised gates give back the tokens: sum_j g[t,j] = 1."""
+    rng = np.random.default_rng(41)
+    n_e, k, T = 9, 4, 30
+    idx = np.stack([rng.choice(n_e, size=k, replace=False) for _ in range(T)])
+    x = rng.standard_normal((T, 6)).astype(np.float32)
+    g = rng.random((T, k))
+    g /= g.sum(axis=1, keepdims=True)
+    _, perm, inv = orc.dispatch_permutation(idx, n_e)
+    y = orc.combine(orc.permute_rows(x, perm, k), g, inv, k)
+    _close(y, x.astype(np.float64), rtol=1e-14, atol=1e-15, what="identity experts")
+
+
+# ------------------------------------------------------------------ backward -------------
+
+def _fd_case(seed, normalize, zc):
+    rng = np.random.default_rng(seed)
+    T, d, n_e, k = 5, 6, 7, 3
+    x = rng.standard_normal((T, d))
+    w = rng.standard_normal((n_e, d)) * 0.5
+    b = rng.standard_normal(n_e) * 0.05
+    G = rng.standard_normal((T, k))
+    return x, w, b, k, G, normalize, zc
+
+
+def pin_backward_finite_differences(orc):
+    """dL/dX and dL/dW against central differences of the loss in float64, at a selection whose
+    margin is far above the step (normalised and raw gates, with and without the z-loss)."""
+    for seed, normalize, zc in ((43, True, 0.0), (47, False, 0.0), (53, True, 0.3), (59, False, 1.0)):
+        x, w, b, k, G, normalize, zc = _fd_case(seed, normalize, zc)
+        grads = orc.router_backward(x, w, b, k, G, normalize=normalize, zloss_coef=zc)
+        assert grads.gap.min() > 1e-4, "pick a seed with a clear selection"
+        h = 1e-6
+        for arr, got in ((x, grads.dx), (w, grads.dw)):
+            num = np.zeros_like(arr)
+            for pos in np.ndindex(arr.shape):
+                old = arr[pos]
+                arr[pos] = old + h
+                lp = orc.router_loss(x, w, grads.idx, G, normalize, zc)
+                arr[pos] = old - h
+                lm = orc.router_loss(x, w, grads.idx, G, normalize, zc)
+                arr[pos] = old
+                num[pos] = (lp - lm) / (2 * h)
+            _close(got, num, rtol=1e-6, atol=1e-8, what=f"finite differences seed {seed}")
+
+
+def pin_backward_uniform_upstream(orc):
+    """Normalised gates sum to 1, so an upstream gradient equal across a token's K slots has zero
+    effect; raw gates instead give dL/dz = G * s (1 - s) at the chosen experts."""
+    x, w, b, k, G, _, _ = _fd_case(61, True, 0.0)
+    Gu = np.repeat(G[:, :1], k, axis=1)
+    grads = orc.router_backward(x, w, b, k, Gu, normalize=True)
+    _close(grads.dz, np.zeros_like(grads.dz), atol=1e-15, what="normalised, uniform upstream")
+    raw = orc.router_backward(x, w, b, k, Gu, normalize=False)
+    z = x @ w.T
+    for t in range(x.shape[0]):
+        for j in range(k):
+            i = int(raw.idx[t, j])
+            s = 1.0 / (1.0 + math.exp(-z[t, i]))
+            _close(raw.dz[t, i], Gu[t, j] * s * (1 - s), rtol=1e-13, what="raw gate derivative")
+        others = [i for i in range(w.shape[0]) if i not in raw.idx[t]]
+        assert (raw.dz[t, others] == 0).all()
+
+
+def pin_backward_zloss_rows(orc):
+    """The z-loss part alone: each token's row of dL/dz sums to c * 2 lse_t / T (softmax sums to 1)."""
+    x, w, b, k, G, _, _ = _fd_case(67, True, 0.0)
+    c = 0.7
+    grads = orc.router_backward(x, w, b, k, np.zeros_like(G), normalize=True, zloss_coef=c)
+    z = x @ w.T
+    T = x.shape[0]
+    for t in range(T):
+        lse = math.log(sum(math.exp(v) for v in z[t]))
+        _close(grads.dz[t].sum(), c * 2 * lse / T, rtol=1e-12, what="z-loss row sum")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

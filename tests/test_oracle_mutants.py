@@ -43,6 +43,21 @@ MUTANTS = [
      "ratio = float(\"inf\") if nmin == 0 else nmax / nbar", "MaxVio over the mean"),
     ("loads.py", "return ratio, (nmax - nbar) / nbar", "return ratio, (nmax - nmin) / nbar", "excess over min"),
     ("zloss.py", "lse = (zmax + np.log(", "lse = (np.log(", "dropped max shift"),
+    ("zloss.py", "return float(np.mean(lse * lse)) if lse.size", "return float(np.mean(lse) ** 2) if lse.size",
+     "square of the mean"),
+    ("balance.py", "balance_step(counts[l], bias[l], momentum[l]", "balance_step(counts[0], bias[l], momentum[l]",
+     "every layer fed layer 0's loads"),
+    ("moe.py", "return x[perm // k]", "return x[perm % len(x)]", "flat index taken as the token"),
+    ("moe.py", "y += g[:, j:j + 1] * eo[rows[:, j]]", "y += g[:, j:j + 1] * eo[rows[:, 0]]", "every slot reads slot 0"),
+    ("moe.py", "rows = np.asarray(inv, dtype=np.int64).reshape(g.shape[0], k)",
+     "rows = np.asarray(inv, dtype=np.int64).reshape(k, g.shape[0]).T", "inv read slot-major"),
+    ("backward.py", "ds = (G - (G * g).sum(axis=1, keepdims=True)) / S", "ds = G / S",
+     "normalisation coupling dropped"),
+    ("backward.py", "dz[rows, idx] = ds * sel * (1.0 - sel)", "dz[rows, idx] = ds * sel", "sigmoid derivative s, not s(1-s)"),
+    ("backward.py", "dz += zloss_coef * (2.0 / T) * lse * p", "dz += zloss_coef * (1.0 / T) * lse * p",
+     "z-loss factor 2 dropped"),
+    ("backward.py", "return RouterGrads(dz=dz, dx=dz @ w64, dw=dz.T @ x64",
+     "return RouterGrads(dz=dz, dx=dz @ w64, dw=dz.T @ x64[::-1]", "tokens reversed in dW"),
 ]
 
 

@@ -120,6 +120,50 @@ def cpu_baseline(wl, x, w, b, m, min_seconds: float = 10.0, max_seconds: float =
             "seconds": round(el, 2)}
 
 
+def time_events(fn, reps: int, stream) -> float:
+    """Average ms of fn() over reps runs, HIP events on `stream` around each."""
+    import torch
+
+    fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / reps
+
+
+def bench_next_rows(elb, wl, x, out, stream, reps: int = 20) -> dict:
+    """The rows beside the hot path, on the same workload and stream: router z-loss reduction,
+    a 60-layer batched bias update, the expert-contiguous permute and the gated combine."""
+    import torch
+
+    T, d, k, n_e = wl.T, wl.d, wl.k, wl.n_experts
+    res = {}
+    lse = torch.randn(T, device=x.device) + 6.0
+    res["zloss_us"] = round(time_events(lambda: elb.zloss(lse), reps, stream) * 1e3, 2)
+    L = 60
+    counts = torch.randint(0, 4 * T // n_e * 2, (L, n_e), dtype=torch.int32, device=x.device)
+    bl, ml = torch.zeros((L, n_e), device=x.device), torch.zeros((L, n_e), device=x.device)
+    res["update_60_layers_us"] = round(time_events(lambda: elb.smebu_update_layers(counts, bl, ml), reps, stream) * 1e3, 2)
+    inv = out.inv_perm.clone()
+    gates = out.gates.clone()
+    xp = torch.empty((T * k, d), dtype=x.dtype, device=x.device)
+    y = torch.empty((T, d), dtype=torch.float32, device=x.device)
+    ms_p = time_events(lambda: elb.permute_rows(x, inv, k, out=xp), reps, stream)
+    ms_c = time_events(lambda: elb.unpermute_combine(xp, gates, inv, out=y), reps, stream)
+    esz = x.element_size()
+    bytes_p = T * d * esz + T * k * d * esz + T * k * 4
+    bytes_c = T * k * d * esz + T * k * 8 + T * d * 4
+    for name, ms, nbytes in (("permute", ms_p, bytes_p), ("combine", ms_c, bytes_c)):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"us": round(ms * 1e3, 2), "alg_bytes": nbytes, "achieved_GBps": round(gbs, 1),
+                     "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -127,6 +171,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="large")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-next", action="store_true", help="skip the rows beside the hot path")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run a device-to-device copy of MIB MiB (the byte-counter reference)")
     ap.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_MIB"),
@@ -232,6 +277,8 @@ def main() -> int:
                          "step": round(ms * 1e3, 2)},
         "maxvio_last": float(mv.cpu()[0]),
     }
+    if not args.no_next:
+        line["next_rows"] = bench_next_rows(elb, wl, xs[0], out, stream)
     if args.calibrate_copy:
         n = args.calibrate_copy * 1024 * 1024
         src = torch.empty(n, dtype=torch.uint8, device=dev)

@@ -40,8 +40,9 @@ from ._lib import (  # noqa: F401
     lib,
 )
 
-__all__ = ["router_forward", "router_dispatch", "dispatch_workspace_bytes", "smebu_update", "maxvio",
-           "RouterStep", "StepOutputs", "version", "ElbError", "MODES"]
+__all__ = ["router_forward", "router_dispatch", "dispatch_workspace_bytes", "smebu_update", "smebu_update_layers",
+           "maxvio", "zloss", "permute_rows", "unpermute_combine", "RouterStep", "StepOutputs", "version", "ElbError",
+           "MODES"]
 
 MODES = {"smebu": ELB_MODE_SMEBU, "sign": ELB_MODE_SIGN, "linear": ELB_MODE_LINEAR}
 _DTYPES = {torch.float32: ELB_F32, torch.bfloat16: ELB_BF16}
@@ -171,6 +172,81 @@ def smebu_update(counts: torch.Tensor, bias: torch.Tensor, momentum: torch.Tenso
     return delta, mv
 
 
+def smebu_update_layers(counts: torch.Tensor, bias: torch.Tensor, momentum: torch.Tensor | None, *,
+                        mode: str = "smebu", lam: float = 5e-4, beta: float = 0.5, kappa: float = 2.0,
+                        gamma: float = 1e-3, want_delta: bool = False, want_maxvio: bool = True,
+                        clear_counts: bool = False):
+    """One update per MoE layer in one launch: counts, bias, momentum are [L, N_r] (each layer's
+    own loads, b and m).  Returns (delta_b [L, N_r] or None, maxvio [L, 2] or None)."""
+    _need(counts, "counts", torch.int32)
+    dev = counts.device
+    _need(bias, "bias", torch.float32, dev)
+    if momentum is not None:
+        _need(momentum, "momentum", torch.float32, dev)
+    if counts.dim() != 2 or bias.shape != counts.shape or (momentum is not None and momentum.shape != counts.shape):
+        raise ValueError("counts, bias and momentum must all be [L, N_r]")
+    if mode not in MODES:
+        raise ValueError(f"mode must be one of {sorted(MODES)}")
+    L, n_e = counts.shape
+    delta = torch.empty((L, n_e), dtype=torch.float32, device=dev) if want_delta else None
+    mv = torch.empty((L, 2), dtype=torch.float32, device=dev) if want_maxvio else None
+    params = BalanceParams(MODES[mode], lam, beta, kappa, gamma, ELB_CLEAR_COUNTS if clear_counts else 0)
+    st = lib().elb_smebu_update_layers(_ptr(counts), L, n_e, params, _ptr(bias), _ptr(momentum), _ptr(delta),
+                                       _ptr(mv), _stream(dev))
+    check("elb_smebu_update_layers", st)
+    return delta, mv
+
+
+def zloss(lse: torch.Tensor) -> torch.Tensor:
+    """mean_t lse_t^2 of per-token log-sum-exps [T], as a device scalar tensor [1]."""
+    _need(lse, "lse", torch.float32)
+    out = torch.empty(1, dtype=torch.float32, device=lse.device)
+    check("elb_zloss", lib().elb_zloss(_ptr(lse), lse.numel(), _ptr(out), _stream(lse.device)))
+    return out
+
+
+def permute_rows(x: torch.Tensor, inv_perm: torch.Tensor, k: int, *, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Expert-contiguous copy of the token rows: out[inv_perm[t*k + j]] = x[t]; out is [T*k, d]."""
+    _need(x, "x")
+    if x.dtype not in _DTYPES:
+        raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
+    dev = x.device
+    _need(inv_perm, "inv_perm", torch.int32, dev)
+    T, d = x.shape
+    if inv_perm.numel() != T * k:
+        raise ValueError(f"inv_perm must hold T*k = {T * k} entries")
+    if out is None:
+        out = torch.empty((T * k, d), dtype=x.dtype, device=dev)
+    else:
+        _need(out, "out", x.dtype, dev)
+    st = lib().elb_permute_rows(_ptr(x), _DTYPES[x.dtype], T, d, k, _ptr(inv_perm), _ptr(out), _stream(dev))
+    check("elb_permute_rows", st)
+    return out
+
+
+def unpermute_combine(expert_out: torch.Tensor, gates: torch.Tensor, inv_perm: torch.Tensor, *,
+                      out_dtype: torch.dtype = torch.float32, out: torch.Tensor | None = None) -> torch.Tensor:
+    """y[t] = sum_j gates[t, j] * expert_out[inv_perm[t*k + j]] (fp32 accumulation); y is [T, d]."""
+    _need(expert_out, "expert_out")
+    if expert_out.dtype not in _DTYPES or out_dtype not in _DTYPES:
+        raise TypeError("expert_out and the output must be float32 or bfloat16")
+    dev = expert_out.device
+    _need(gates, "gates", torch.float32, dev)
+    _need(inv_perm, "inv_perm", torch.int32, dev)
+    T, k = gates.shape
+    d = expert_out.shape[1]
+    if expert_out.shape[0] != T * k or inv_perm.numel() != T * k:
+        raise ValueError("expert_out and inv_perm must hold T*k rows")
+    if out is None:
+        out = torch.empty((T, d), dtype=out_dtype, device=dev)
+    else:
+        _need(out, "out", out_dtype, dev)
+    st = lib().elb_unpermute_combine(_ptr(expert_out), _DTYPES[expert_out.dtype], T, d, k, _ptr(inv_perm),
+                                     _ptr(gates), _ptr(out), _DTYPES[out_dtype], _stream(dev))
+    check("elb_unpermute_combine", st)
+    return out
+
+
 def maxvio(counts: torch.Tensor) -> torch.Tensor:
     """[max n / min n, (max n - nbar) / nbar] of one step's loads, as a device tensor."""
     _need(counts, "counts", torch.int32)
@@ -189,6 +265,7 @@ class StepOutputs(NamedTuple):
     perm: torch.Tensor       # [T * k] int32
     inv_perm: torch.Tensor | None
     lse: torch.Tensor | None
+    zloss: torch.Tensor | None
     delta_b: torch.Tensor | None
     maxvio: torch.Tensor | None
 
@@ -207,8 +284,8 @@ class RouterStep:
     def __init__(self, w: torch.Tensor, bias: torch.Tensor, momentum: torch.Tensor | None, k: int, max_tokens: int,
                  *, update: bool = True, mode: str = "smebu", lam: float = 5e-4, beta: float = 0.5,
                  kappa: float = 2.0, gamma: float = 1e-3, clear_counts: bool = True, gates_raw: bool = False,
-                 want_inv: bool = True, want_lse: bool = False, want_delta: bool = False, want_maxvio: bool = True,
-                 force_generic: bool = False):
+                 want_inv: bool = True, want_lse: bool = False, want_zloss: bool = False, want_delta: bool = False,
+                 want_maxvio: bool = True, force_generic: bool = False):
         _need(w, "w")
         dev = w.device
         if w.dtype not in _DTYPES:
@@ -230,7 +307,8 @@ class RouterStep:
         self.offsets = torch.empty(n_e + 1, dtype=i32, device=dev)
         self.perm = torch.empty(T * k, dtype=i32, device=dev)
         self.inv_perm = torch.empty(T * k, dtype=i32, device=dev) if want_inv else None
-        self.lse = torch.empty(T, dtype=f32, device=dev) if want_lse else None
+        self.lse = torch.empty(T, dtype=f32, device=dev) if (want_lse or want_zloss) else None
+        self.zloss = torch.empty(1, dtype=f32, device=dev) if want_zloss else None
         self.delta_b = torch.empty(n_e, dtype=f32, device=dev) if (update and want_delta) else None
         self.maxvio = torch.empty(2, dtype=f32, device=dev) if (update and want_maxvio) else None
         ws_bytes = dispatch_workspace_bytes(T, k, n_e)
@@ -240,7 +318,7 @@ class RouterStep:
         a.dtype, a.d, a.w, a.bias = _DTYPES[w.dtype], d, w.data_ptr(), bias.data_ptr()
         a.n_experts, a.k, a.flags = n_e, k, flags
         a.topk_idx, a.gates, a.counts = self.topk_idx.data_ptr(), self.gates.data_ptr(), self.counts.data_ptr()
-        a.logits, a.lse = None, _ptr(self.lse).value
+        a.logits, a.lse, a.zloss = None, _ptr(self.lse).value, _ptr(self.zloss).value
         a.workspace, a.workspace_bytes = self.workspace.data_ptr(), self.workspace.numel()
         a.offsets, a.perm, a.inv_perm = self.offsets.data_ptr(), self.perm.data_ptr(), _ptr(self.inv_perm).value
         a.update = 1 if update else 0
@@ -272,4 +350,4 @@ class RouterStep:
         k = self.k
         return StepOutputs(self.topk_idx[:T], self.gates[:T], self.counts, self.offsets, self.perm[:T * k],
                            None if self.inv_perm is None else self.inv_perm[:T * k],
-                           None if self.lse is None else self.lse[:T], self.delta_b, self.maxvio)
+                           None if self.lse is None else self.lse[:T], self.zloss, self.delta_b, self.maxvio)

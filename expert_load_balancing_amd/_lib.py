@@ -34,7 +34,7 @@ class StepArgs(ctypes.Structure):
     _fields_ = [
         ("x", _P), ("dtype", _I32), ("T", _I64), ("d", _I32), ("w", _P), ("bias", _P), ("n_experts", _I32),
         ("k", _I32), ("flags", _U32), ("topk_idx", _P), ("gates", _P), ("counts", _P), ("logits", _P), ("lse", _P),
-        ("workspace", _P), ("workspace_bytes", _SZ), ("offsets", _P), ("perm", _P), ("inv_perm", _P),
+        ("zloss", _P), ("workspace", _P), ("workspace_bytes", _SZ), ("offsets", _P), ("perm", _P), ("inv_perm", _P),
         ("update", _I32), ("params", BalanceParams), ("momentum", _P), ("delta_b", _P), ("maxvio", _P),
         ("timing", _P),
     ]
@@ -46,6 +46,10 @@ SIGNATURES = {
     "elb_router_dispatch": (_I32, [_P, _I64, _I32, _I32, _P, _SZ, _P, _P, _P, _P]),
     "elb_smebu_update": (_I32, [_P, _I32, BalanceParams, _P, _P, _P, _P, _P]),
     "elb_route_step": (_I32, [ctypes.POINTER(StepArgs), _P]),
+    "elb_smebu_update_layers": (_I32, [_P, _I32, _I32, BalanceParams, _P, _P, _P, _P, _P]),
+    "elb_zloss": (_I32, [_P, _I64, _P, _P]),
+    "elb_permute_rows": (_I32, [_P, _I32, _I64, _I32, _I32, _P, _P, _P]),
+    "elb_unpermute_combine": (_I32, [_P, _I32, _I64, _I32, _I32, _P, _P, _P, _I32, _P]),
     "elb_maxvio": (_I32, [_P, _I32, _P, _P]),
     "elb_status_str": (ctypes.c_char_p, [_I32]),
     "elb_version": (ctypes.c_int, []),

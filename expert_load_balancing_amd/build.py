@@ -23,7 +23,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libelb.so")
 ARCH = "gfx950"
 
-SOURCES = ["elb_api.cpp", "util.hip", "balance.hip", "dispatch.hip", "router_generic.hip", "router_mfma.hip"]
+SOURCES = ["elb_api.cpp", "util.hip", "balance.hip", "dispatch.hip", "moe_ops.hip", "router_generic.hip",
+           "router_mfma.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

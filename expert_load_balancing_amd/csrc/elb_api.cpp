@@ -122,6 +122,8 @@ elb_status elb_route_step(const elb_step_args* args, elb_stream_t stream) {
     if (st != ELB_OK) return st;
   }
   if (a.timing != nullptr && (a.timing[0] == nullptr || a.timing[1] == nullptr)) return ELB_ERR_NULL;
+  if (a.zloss != nullptr && a.lse == nullptr) return ELB_ERR_NULL;
+  if (!aligned(a.zloss, 4)) return ELB_ERR_ALIGN;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (!(a.flags & ELB_ACCUMULATE_COUNTS)) {
@@ -141,10 +143,51 @@ elb_status elb_route_step(const elb_step_args* args, elb_stream_t stream) {
   }
   if (a.timing != nullptr && hipEventRecord(static_cast<hipEvent_t>(a.timing[1]), s) != hipSuccess)
     return ELB_ERR_LAUNCH;
+  if (a.zloss != nullptr && elb::launch_zloss(a.lse, a.T, a.zloss, s) != hipSuccess) return ELB_ERR_LAUNCH;
   const elb::BalanceArgs upd =
       balance_args(a.counts, a.n_experts, a.params, a.bias, a.momentum, a.delta_b, a.maxvio);
   return from_hip(elb::launch_dispatch(a.topk_idx, a.T, a.k, a.n_experts, a.workspace, mfma,
                                        a.update != 0 ? &upd : nullptr, a.offsets, a.perm, a.inv_perm, s));
+}
+
+elb_status elb_smebu_update_layers(int32_t* counts, int32_t n_layers, int32_t n_experts, elb_balance_params params,
+                                   float* bias, float* momentum, float* delta_b, float* maxvio, elb_stream_t stream) {
+  const elb_status st = check_update(counts, n_experts, params, bias, momentum, delta_b, maxvio);
+  if (st != ELB_OK) return st;
+  if (n_layers < 1 || (int64_t)n_layers * n_experts >= (int64_t(1) << 31)) return ELB_ERR_SHAPE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return from_hip(
+      elb::launch_balance_layers(balance_args(counts, n_experts, params, bias, momentum, delta_b, maxvio), n_layers, s));
+}
+
+elb_status elb_zloss(const float* lse, int64_t T, float* out, elb_stream_t stream) {
+  if (out == nullptr || (T > 0 && lse == nullptr)) return ELB_ERR_NULL;
+  if (T < 0) return ELB_ERR_SHAPE;
+  if (!aligned(lse, 4) || !aligned(out, 4)) return ELB_ERR_ALIGN;
+  return from_hip(elb::launch_zloss(lse, T, out, reinterpret_cast<hipStream_t>(stream)));
+}
+
+elb_status elb_permute_rows(const void* x, int32_t dtype, int64_t T, int32_t d, int32_t k, const int32_t* inv_perm,
+                            void* x_perm, elb_stream_t stream) {
+  if (T > 0 && (x == nullptr || inv_perm == nullptr || x_perm == nullptr)) return ELB_ERR_NULL;
+  if (dtype != ELB_F32 && dtype != ELB_BF16) return ELB_ERR_UNSUPPORTED;
+  if (T < 0 || d < 1 || k < 1 || k > 8 || T * (int64_t)k >= (int64_t(1) << 31)) return ELB_ERR_SHAPE;
+  const int64_t row_bytes = (int64_t)d * (dtype == ELB_F32 ? 4 : 2);
+  if (row_bytes % 16 != 0 || !aligned(x, 16) || !aligned(x_perm, 16) || !aligned(inv_perm, 4)) return ELB_ERR_ALIGN;
+  return from_hip(elb::launch_permute_rows(x, T, row_bytes, k, inv_perm, x_perm, reinterpret_cast<hipStream_t>(stream)));
+}
+
+elb_status elb_unpermute_combine(const void* expert_out, int32_t dtype, int64_t T, int32_t d, int32_t k,
+                                 const int32_t* inv_perm, const float* gates, void* y, int32_t y_dtype,
+                                 elb_stream_t stream) {
+  if (T > 0 && (expert_out == nullptr || inv_perm == nullptr || gates == nullptr || y == nullptr)) return ELB_ERR_NULL;
+  if ((dtype != ELB_F32 && dtype != ELB_BF16) || (y_dtype != ELB_F32 && y_dtype != ELB_BF16))
+    return ELB_ERR_UNSUPPORTED;
+  if (T < 0 || d < 1 || k < 1 || k > 8 || T * (int64_t)k >= (int64_t(1) << 31)) return ELB_ERR_SHAPE;
+  if (d % (dtype == ELB_BF16 ? 8 : 4) != 0) return ELB_ERR_ALIGN;
+  if (!aligned(expert_out, 16) || !aligned(y, 16) || !aligned(inv_perm, 4) || !aligned(gates, 4)) return ELB_ERR_ALIGN;
+  return from_hip(elb::launch_combine(expert_out, dtype, T, d, k, inv_perm, gates, y, y_dtype,
+                                      reinterpret_cast<hipStream_t>(stream)));
 }
 
 elb_status elb_maxvio(const int32_t* counts, int32_t n_experts, float* out, elb_stream_t stream) {

@@ -78,5 +78,14 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t T, int k, int n_experts, 
                            hipStream_t stream);
 
 hipError_t launch_balance(const BalanceArgs& a, hipStream_t stream);
+// n_layers independent updates, layer l at offset l * a.n (maxvio at 2 l).
+hipError_t launch_balance_layers(const BalanceArgs& a, int n_layers, hipStream_t stream);
+hipError_t launch_zloss(const float* lse, int64_t T, float* out, hipStream_t stream);
+
+// moe_ops.hip: row_bytes % 16 == 0; x, xp, eo, y 16-byte aligned.
+hipError_t launch_permute_rows(const void* x, int64_t T, int64_t row_bytes, int k, const int32_t* inv, void* xp,
+                               hipStream_t stream);
+hipError_t launch_combine(const void* eo, int in_dtype, int64_t T, int d, int k, const int32_t* inv,
+                          const float* gates, void* y, int out_dtype, hipStream_t stream);
 
 }  // namespace elb

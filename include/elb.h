@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define ELB_VERSION 10100 /* major * 10000 + minor * 100 + patch */
+#define ELB_VERSION 10200 /* major * 10000 + minor * 100 + patch */
 
 typedef struct ihipStream_t* elb_stream_t; /* hipStream_t; NULL = default stream */
 
@@ -180,6 +180,7 @@ typedef struct {
   int32_t* counts;
   float* logits;
   float* lse;
+  float* zloss; /* [1] out, or NULL: elb_zloss of this batch's lse (lse must then be given) */
   /* elb_router_dispatch */
   void* workspace;
   size_t workspace_bytes;
@@ -197,6 +198,57 @@ typedef struct {
 } elb_step_args;
 
 elb_status elb_route_step(const elb_step_args* args, elb_stream_t stream);
+
+/*
+ * Bias updates of n_layers MoE layers in one launch, each from its own loads: the arguments of
+ * elb_smebu_update stacked layer-major.  counts, bias, momentum, delta_b are [n_layers][n_experts]
+ * and maxvio is [n_layers][2] (per-layer MaxVio telemetry).  Layer l's result is exactly what
+ * elb_smebu_update gives on layer l's rows; layers do not interact (the update is stated per
+ * router: "SMEBU Load Balancing", "How it works").  Supported: n_layers >= 1,
+ * 1 <= n_experts <= 1024, n_layers * n_experts < 2^31.  Errors as elb_smebu_update.
+ */
+elb_status elb_smebu_update_layers(int32_t* counts, int32_t n_layers, int32_t n_experts, elb_balance_params params,
+                                   float* bias, float* momentum, float* delta_b, float* maxvio,
+                                   elb_stream_t stream);
+
+/*
+ * Router z-loss of one batch from the per-token log-sum-exps of elb_router_forward:
+ *   out[0] = mean_t lse[t]^2   (0 when T == 0)
+ * (talk summary "Arcee Halts 400B Blackwell Model Collapse...", section "Precision Fallbacks,
+ * Loss Stabilization, and MaxVio ..."; the weight is applied by the caller).  Summed in
+ * float64 in a fixed order: deterministic.  Errors: ELB_ERR_NULL, ELB_ERR_SHAPE (T < 0),
+ * ELB_ERR_ALIGN, ELB_ERR_LAUNCH.
+ */
+elb_status elb_zloss(const float* lse, int64_t T, float* out, elb_stream_t stream);
+
+/*
+ * Expert-contiguous copy of the token rows (the gather before the routed experts):
+ *   x_perm[inv_perm[t * k + j]] = x[t]   for every token t and slot j,
+ * so rows offsets[e] .. offsets[e+1] of x_perm are expert e's tokens, in the order of
+ * elb_router_dispatch's perm.  Rows are copied bit for bit.
+ *   x       [T, d] of `dtype` (fp32 or bf16), row-major; every row 16-byte aligned.
+ *   inv_perm[T * k] int32: a permutation of 0 .. T*k-1 (elb_router_dispatch's inv_perm).
+ *   x_perm  [T * k, d] of `dtype` out.
+ * Each token row is read once.  Errors: ELB_ERR_NULL, ELB_ERR_SHAPE, ELB_ERR_UNSUPPORTED
+ * (dtype), ELB_ERR_ALIGN, ELB_ERR_LAUNCH.
+ */
+elb_status elb_permute_rows(const void* x, int32_t dtype, int64_t T, int32_t d, int32_t k, const int32_t* inv_perm,
+                            void* x_perm, elb_stream_t stream);
+
+/*
+ * Gated combine of the routed experts' outputs back to token order (Arcee Trinity Large
+ * Technical Report, section 2.3: the gating scores weight the routed experts' outputs):
+ *   y[t] = sum_{j=0}^{k-1} gates[t, j] * expert_out[inv_perm[t * k + j]]
+ * accumulated in fp32 in slot order with fused multiply-adds.
+ *   expert_out [T * k, d] of `dtype` (fp32 or bf16), rows in expert-contiguous order.
+ *   gates      [T, k] fp32 (elb_router_forward's gates).
+ *   y          [T, d] out, fp32 or bf16 (y_dtype; bf16 rounds to nearest even).
+ * d % 8 == 0 for bf16 expert_out, d % 4 == 0 for fp32; pointers 16-byte aligned.  Errors:
+ * ELB_ERR_NULL, ELB_ERR_SHAPE, ELB_ERR_UNSUPPORTED, ELB_ERR_ALIGN, ELB_ERR_LAUNCH.
+ */
+elb_status elb_unpermute_combine(const void* expert_out, int32_t dtype, int64_t T, int32_t d, int32_t k,
+                                 const int32_t* inv_perm, const float* gates, void* y, int32_t y_dtype,
+                                 elb_stream_t stream);
 
 /*
  * MaxVio of one step's loads: out[0] = max n / min n (the talk's definition, section

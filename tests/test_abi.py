@@ -175,3 +175,53 @@ def test_struct_layout_matches_header(cls, cname, tmp_path):
     for f, cf in zip(names, c_names):
         assert getattr(cls, f).offset == got[cf], (cname, cf)
     assert ctypes.sizeof(cls) == got["sizeof"]
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(counts=None), NULL), (dict(bias=None), NULL), (dict(momentum=None), NULL), (dict(L=0), SHAPE),
+    (dict(L=-3), SHAPE), (dict(n=0), SHAPE), (dict(n=1025), SHAPE), (dict(L=1 << 22, n=1024), SHAPE),
+    (dict(mode=9), UNSUPPORTED), (dict(flags=8), UNSUPPORTED), (dict(mv=FAKE + 2), ALIGN),
+])
+def test_smebu_update_layers_rejects(lib, kw, want):
+    a = dict(counts=FAKE, L=60, n=256, mode=0, bias=FAKE, momentum=FAKE, delta=None, mv=None, flags=0)
+    a.update(kw)
+    p = _lib.BalanceParams(a["mode"], 5e-4, 0.5, 2.0, 1e-3, a["flags"])
+    st = lib.elb_smebu_update_layers(a["counts"], a["L"], a["n"], p, a["bias"], a["momentum"], a["delta"], a["mv"],
+                                     None)
+    assert st == want
+
+
+def test_zloss_rejects(lib):
+    assert lib.elb_zloss(FAKE, 100, None, None) == NULL
+    assert lib.elb_zloss(None, 100, FAKE, None) == NULL
+    assert lib.elb_zloss(FAKE, -1, FAKE, None) == SHAPE
+    assert lib.elb_zloss(FAKE + 2, 100, FAKE, None) == ALIGN
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=None), NULL), (dict(inv=None), NULL), (dict(xp=None), NULL), (dict(dtype=3), UNSUPPORTED),
+    (dict(T=-1), SHAPE), (dict(d=0), SHAPE), (dict(k=0), SHAPE), (dict(k=9), SHAPE), (dict(T=1 << 29, k=4), SHAPE),
+    (dict(d=100), ALIGN), (dict(dtype=0, d=98), ALIGN), (dict(x=FAKE + 8), ALIGN), (dict(xp=FAKE + 4), ALIGN),
+])
+def test_permute_rows_rejects(lib, kw, want):
+    a = dict(x=FAKE, dtype=1, T=1000, d=256, k=4, inv=FAKE, xp=FAKE)
+    a.update(kw)
+    assert lib.elb_permute_rows(a["x"], a["dtype"], a["T"], a["d"], a["k"], a["inv"], a["xp"], None) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(eo=None), NULL), (dict(inv=None), NULL), (dict(g=None), NULL), (dict(y=None), NULL),
+    (dict(dtype=2), UNSUPPORTED), (dict(ydt=5), UNSUPPORTED), (dict(T=-2), SHAPE), (dict(k=9), SHAPE),
+    (dict(d=100), ALIGN), (dict(dtype=0, d=102), ALIGN), (dict(y=FAKE + 8), ALIGN), (dict(g=FAKE + 1), ALIGN),
+])
+def test_unpermute_combine_rejects(lib, kw, want):
+    a = dict(eo=FAKE, dtype=1, T=1000, d=256, k=4, inv=FAKE, g=FAKE, y=FAKE, ydt=0)
+    a.update(kw)
+    st = lib.elb_unpermute_combine(a["eo"], a["dtype"], a["T"], a["d"], a["k"], a["inv"], a["g"], a["y"], a["ydt"],
+                                   None)
+    assert st == want
+
+
+def test_route_step_zloss_needs_lse(lib):
+    a = step_args(zloss=FAKE, lse=None)
+    assert lib.elb_route_step(ctypes.byref(a), None) == NULL

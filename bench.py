@@ -135,9 +135,10 @@ def time_events(fn, reps: int, stream) -> float:
     return sum(a.elapsed_time(b) for a, b in ev) / reps
 
 
-def bench_next_rows(elb, wl, x, out, stream, reps: int = 20) -> dict:
+def bench_next_rows(elb, wl, x, w, out, stream, reps: int = 20) -> dict:
     """The rows beside the hot path, on the same workload and stream: router z-loss reduction,
-    a 60-layer batched bias update, the expert-contiguous permute and the gated combine."""
+    a 60-layer batched bias update, the router backward, the expert-contiguous permute and the
+    gated combine."""
     import torch
 
     T, d, k, n_e = wl.T, wl.d, wl.k, wl.n_experts
@@ -154,6 +155,14 @@ def bench_next_rows(elb, wl, x, out, stream, reps: int = 20) -> dict:
     y = torch.empty((T, d), dtype=torch.float32, device=x.device)
     ms_p = time_events(lambda: elb.permute_rows(x, inv, k, out=xp), reps, stream)
     ms_c = time_events(lambda: elb.unpermute_combine(xp, gates, inv, out=y), reps, stream)
+    # Router backward with the z-loss (recomputed logits, dL/dz, dX = dZ W, dW = dZ^T X).
+    dg = torch.randn((T, k), device=x.device)
+    ws_b = torch.empty(elb.backward_workspace_bytes(T, d, n_e), dtype=torch.uint8, device=x.device)
+    ms_b = time_events(lambda: elb.router_backward(x, w, out.topk_idx, dg, zloss_coef=1e-3, workspace=ws_b),
+                       max(3, reps // 4), stream)
+    fl = 3 * 2.0 * T * n_e * d
+    res["backward"] = {"us": round(ms_b * 1e3, 2), "flops": fl, "tflops": round(fl / (ms_b * 1e-3) / 1e12, 1),
+                       "mfma_frac": round(fl / (ms_b * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
     esz = x.element_size()
     bytes_p = T * d * esz + T * k * d * esz + T * k * 4
     bytes_c = T * k * d * esz + T * k * 8 + T * d * 4
@@ -278,7 +287,7 @@ def main() -> int:
         "maxvio_last": float(mv.cpu()[0]),
     }
     if not args.no_next:
-        line["next_rows"] = bench_next_rows(elb, wl, xs[0], out, stream)
+        line["next_rows"] = bench_next_rows(elb, wl, xs[0], wd, out, stream)
     if args.calibrate_copy:
         n = args.calibrate_copy * 1024 * 1024
         src = torch.empty(n, dtype=torch.uint8, device=dev)

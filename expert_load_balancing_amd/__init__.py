@@ -41,7 +41,7 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = ["router_forward", "router_dispatch", "dispatch_workspace_bytes", "smebu_update", "smebu_update_layers",
-           "maxvio", "zloss", "permute_rows", "unpermute_combine", "RouterStep", "StepOutputs", "version", "ElbError",
+           "maxvio", "zloss", "permute_rows", "unpermute_combine", "router_backward", "backward_workspace_bytes", "RouterStep", "StepOutputs", "version", "ElbError",
            "MODES"]
 
 MODES = {"smebu": ELB_MODE_SMEBU, "sign": ELB_MODE_SIGN, "linear": ELB_MODE_LINEAR}
@@ -245,6 +245,39 @@ def unpermute_combine(expert_out: torch.Tensor, gates: torch.Tensor, inv_perm: t
                                      _ptr(gates), _ptr(out), _DTYPES[out_dtype], _stream(dev))
     check("elb_unpermute_combine", st)
     return out
+
+
+def backward_workspace_bytes(T: int, d: int, n_experts: int) -> int:
+    return int(lib().elb_backward_workspace_bytes(T, d, n_experts))
+
+
+def router_backward(x: torch.Tensor, w: torch.Tensor, topk_idx: torch.Tensor, dgates: torch.Tensor, *,
+                    gates_raw: bool = False, zloss_coef: float = 0.0, want_dx: bool = True, want_dw: bool = True,
+                    workspace: torch.Tensor | None = None):
+    """Gradients of sum(dgates * gates) + zloss_coef * mean(lse^2) at the selection topk_idx:
+    returns (dx [T, d] fp32 or None, dw [N_r, d] fp32 or None).  bf16 x and w, d % 64 == 0."""
+    _need(x, "x", torch.bfloat16)
+    dev = x.device
+    _need(w, "w", torch.bfloat16, dev)
+    _need(topk_idx, "topk_idx", torch.int32, dev)
+    _need(dgates, "dgates", torch.float32, dev)
+    T, d = x.shape
+    n_e = w.shape[0]
+    k = topk_idx.shape[1]
+    if w.shape[1] != d or topk_idx.shape[0] != T or dgates.shape != topk_idx.shape:
+        raise ValueError("shapes do not match")
+    need = backward_workspace_bytes(T, d, n_e)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    else:
+        _need(workspace, "workspace", device=dev)
+    dx = torch.empty((T, d), dtype=torch.float32, device=dev) if want_dx else None
+    dw = torch.empty((n_e, d), dtype=torch.float32, device=dev) if want_dw else None
+    st = lib().elb_router_backward(_ptr(x), ELB_BF16, T, d, _ptr(w), n_e, k, ELB_GATES_RAW if gates_raw else 0,
+                                   _ptr(topk_idx), _ptr(dgates), float(zloss_coef), _ptr(dx), _ptr(dw),
+                                   _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
+    check("elb_router_backward", st)
+    return dx, dw
 
 
 def maxvio(counts: torch.Tensor) -> torch.Tensor:

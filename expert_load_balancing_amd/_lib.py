@@ -50,6 +50,8 @@ SIGNATURES = {
     "elb_zloss": (_I32, [_P, _I64, _P, _P]),
     "elb_permute_rows": (_I32, [_P, _I32, _I64, _I32, _I32, _P, _P, _P]),
     "elb_unpermute_combine": (_I32, [_P, _I32, _I64, _I32, _I32, _P, _P, _P, _I32, _P]),
+    "elb_backward_workspace_bytes": (_SZ, [_I64, _I32, _I32]),
+    "elb_router_backward": (_I32, [_P, _I32, _I64, _I32, _P, _I32, _I32, _U32, _P, _P, _F, _P, _P, _P, _SZ, _P]),
     "elb_maxvio": (_I32, [_P, _I32, _P, _P]),
     "elb_status_str": (ctypes.c_char_p, [_I32]),
     "elb_version": (ctypes.c_int, []),

@@ -24,7 +24,7 @@ LIB = os.path.join(PKG, "libelb.so")
 ARCH = "gfx950"
 
 SOURCES = ["elb_api.cpp", "util.hip", "balance.hip", "dispatch.hip", "moe_ops.hip", "router_generic.hip",
-           "router_mfma.hip"]
+           "router_mfma.hip", "router_backward.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -82,6 +82,35 @@ hipError_t launch_balance(const BalanceArgs& a, hipStream_t stream);
 hipError_t launch_balance_layers(const BalanceArgs& a, int n_layers, hipStream_t stream);
 hipError_t launch_zloss(const float* lse, int64_t T, float* out, hipStream_t stream);
 
+// router_backward.hip (bf16, d % 64 == 0).
+struct BackwardArgs {
+  const void* x;
+  int64_t T;
+  int d;
+  const void* w;
+  int n_experts;
+  int k;
+  int normalize;
+  const int32_t* idx;
+  const float* dgates;
+  float zloss_coef;
+  float* dx;  // [T][d] fp32, or NULL
+  float* dw;  // [n_experts][d] fp32, or NULL
+};
+struct BackwardPlan {
+  int64_t T_pad;    // T rounded up to the 256-token tile (at least one tile)
+  int64_t k_chunk;  // tokens per dW partial
+  int splits;       // number of dW partials
+  uint16_t* dzt;    // dL/dz, expert-major [256][T_pad] bf16
+  uint16_t* dz;     // dL/dz, token-major [T_pad][256] bf16
+  uint16_t* wt;     // W^T [d][256] bf16
+  uint16_t* xt;     // X^T [d][T_pad] bf16
+  float* part;      // dW partials [splits][256][d] fp32
+  size_t bytes;     // workspace bytes
+};
+BackwardPlan backward_plan(int64_t T, int d, void* workspace);  // workspace may be NULL (sizes only)
+hipError_t launch_router_backward(const BackwardArgs& a, const BackwardPlan& p, hipStream_t stream);
+
 // moe_ops.hip: row_bytes % 16 == 0; x, xp, eo, y 16-byte aligned.
 hipError_t launch_permute_rows(const void* x, int64_t T, int64_t row_bytes, int k, const int32_t* inv, void* xp,
                                hipStream_t stream);

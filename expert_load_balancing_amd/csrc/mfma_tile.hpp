@@ -1,0 +1,242 @@
+// One workgroup's 256 x 256 fp32 product tile on CDNA4 matrix cores (gfx950):
+//   acc[m][n] = sum_k A[m][k] * B[n][k]        m, n < 256; A, B bf16, rows contiguous in k
+// held in registers, with both operands streamed from memory into LDS by buffer-to-LDS DMA.
+// The router forward uses it with A = the router weights and B = a tile of tokens (the logits,
+// transposed: Z^T = W X^T); the router backward uses it for its two weight-side products.
+//
+// Work decomposition: 4 waves, one per SIMD; wave w owns B rows 64 w .. 64 w + 63 against all
+// 256 A rows, i.e. 8 x 2 accumulators of 32 x 32 (256 AGPRs).  A 32 x 32 MFMA output puts one
+// B row per lane column: lane l holds column l % 32 of its block, and accumulator r holds A row
+// 8 (r / 4) + 4 (l / 32) + (r % 4).
+//
+// Memory pipeline: k is consumed in stages of 64 elements (128 bytes of every row: a full HBM
+//   line per row per visit; 64-byte visits stream markedly slower because all workgroups touch
+//   their rows 2*K bytes apart at once).  The B stream runs 2 stages ahead in a ring of 3 LDS
+//   slots, the A stream 1 stage ahead in a ring of 2 (A is meant to be the operand that stays in
+//   L2, well within one stage).  The five 32 KiB slots fill the 160 KiB LDS.  Rows past the end
+//   of an operand fall outside its buffer range and arrive as zeros.  Every wave waits for its
+//   own DMAs with an explicit vmcnt budget, then one barrier per stage publishes the slot to all
+//   waves and frees the slot the next DMA overwrites.  Barriers carry no memory fence: a fence
+//   on LDS would wait for every DMA in flight and drain the prefetch.  Near the end, dummy DMAs
+//   through an empty-range descriptor keep the vmcnt budget uniform; they move no bytes.  Within
+//   a slot, the eight 16-byte chunks of row r sit at chunk ^ ((r >> 1) & 7), which keeps the
+//   MFMA operand reads (16 rows x 16 bytes per LDS cycle over 64 banks) free of bank conflicts.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace elb {
+namespace tile {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kRowsA = 256;               // A rows per tile
+constexpr int kMB = kRowsA / 32;          // 32-row MFMA blocks of A
+constexpr int kRowsWave = 64;             // B rows per wave
+constexpr int kNB = kRowsWave / 32;       // 32-column MFMA blocks of B
+constexpr int kRowsB = kWaves * kRowsWave;  // B rows per tile
+constexpr int kBK = 64;                   // k elements per stage
+constexpr int kRowB = kBK * 2;            // bytes of one row per stage
+constexpr int kSlot = 256 * kRowB;        // one stage of 256 rows: 32 KiB
+constexpr int kNX = 3, kPX = 2;           // B ring: slots, stages in flight
+constexpr int kNW = 2, kPW = 1;           // A ring
+constexpr int kUnroll = 6;                // lcm(kNX, kNW): slots are compile-time constants
+constexpr int kKSteps = kBK / 16;         // MFMA k-steps per stage
+// The compiler tracks at most 8 distinct LDS DMA targets when it decides which DMAs an LDS
+// read must wait for; with more slots it would fall back to waiting for all of them.
+static_assert(kNX + kNW <= 8, "at most 8 DMA target slots");
+static_assert((kNX + kNW) * kSlot <= 160 * 1024, "LDS");
+constexpr int kDma = kSlot / (kWaves * 1024);  // DMA instructions per wave per slot (1 KiB each)
+
+static_assert(kNX == kPX + 1 && kNW == kPW + 1 && kUnroll % kNX == 0 && kUnroll % kNW == 0, "ring shape");
+static_assert(kPX >= kPW, "the vmcnt budget below assumes the B stream runs further ahead");
+// VMEM instructions a wave issues after the DMAs of stage j's A rows, when it must have stage j:
+// the B DMAs of the same iteration, then (kPW - 1) full iterations.
+constexpr int kVmBudget = kDma + 2 * kDma * (kPW - 1);
+
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitLgkm0 = 63 & 15 | (3 << 14) | (7 << 4);  // lgkmcnt(0) only
+
+// Cache policies of the DMAs.  A stream read exactly once goes non-temporal (nt): streaming it
+// through the caches with normal allocation costs an L2-resident operand its place (for the
+// router forward, the whole memory pipeline ~20% of its rate).
+constexpr int kAuxStream = 2;  // nt
+constexpr int kAuxCached = 0;  // default allocation
+
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // Raw buffer: stride 0, range checked against `bytes`; out-of-range loads return zeros.
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+#define ELB_AS3(p) ((__attribute__((address_space(3))) void*)(p))
+
+// One wave's share of one slot: kDma 1-KiB DMA instructions (8 rows each).  A dummy DMA (past
+// the last stage) keeps the vmcnt budget uniform: it goes through `none`, a descriptor with an
+// empty range, so it reads zeros and moves no bytes.  The choice is a scalar select of the
+// descriptor; the row offsets stay in their own registers.  (Selecting the offset per DMA
+// instead put a VALU write to one shared register before every DMA, which stalls behind the
+// previous DMA's operand read whenever the vector memory queue is full, and with it every
+// MFMA queued behind.)
+template <int AUX>
+__device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, __amdgpu_buffer_rsrc_t none,
+                                         unsigned char* wave_base, const uint32_t (&vo)[kDma], uint32_t soff,
+                                         bool real) {
+  const __amdgpu_buffer_rsrc_t use = real ? r : none;
+#pragma unroll
+  for (int i = 0; i < kDma; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(use, ELB_AS3(wave_base + i * 1024), 16, vo[i], (int)soff, 0, AUX);
+}
+
+// LDS position of 16-byte chunk c of a 128-byte row segment r.  The LDS serves 16 lanes x 16
+// bytes per cycle from 64 banks; an MFMA operand read has 16 consecutive rows read the same
+// chunk, and XOR-ing the chunk with bits 1..3 of the row spreads those 16 reads over the
+// whole 256-byte bank window (rows r and r + 1 already sit in different 128-byte halves).
+__device__ __forceinline__ constexpr int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+// The five LDS slots (declared __shared__ by the kernel, each kSlot bytes, 1 KiB aligned).
+struct Slots {
+  unsigned char *x0, *x1, *x2, *w0, *w1;
+  __device__ __forceinline__ unsigned char* x(int i) const { return i == 0 ? x0 : i == 1 ? x1 : x2; }
+  __device__ __forceinline__ unsigned char* w(int i) const { return i == 0 ? w0 : w1; }
+};
+
+// The streaming product.  AUX_A / AUX_B: cache policies of the two streams.  Both operands'
+// rows are `row_bytes` apart; `nkb` stages of kBK elements are contracted (nkb >= 1).
+template <int AUX_A, int AUX_B>
+struct Stream {
+  __amdgpu_buffer_rsrc_t ar, br, none;
+  uint32_t vo[kDma];
+  uint32_t wave_off;
+  int nkb;
+  Slots sl;
+
+  // a_bytes / b_bytes: the readable bytes of each operand from its base (rows past them read 0).
+  __device__ __forceinline__ void init(const void* a, uint32_t a_bytes, const void* b, uint32_t b_bytes,
+                                       uint32_t row_bytes, int n_stages, int wave, int lane, Slots slots) {
+    ar = make_rsrc(a, a_bytes);
+    br = make_rsrc(b, b_bytes);
+    none = make_rsrc(a, 0u);
+    nkb = n_stages;
+    sl = slots;
+    // DMA lane mapping: instruction i of wave `wave` fills rows wave*64 + 8 i + lane/8; lane
+    // position p = lane & 7 in the row receives the global chunk stored there, swz(row, p)
+    // (the swizzle is its own inverse).
+#pragma unroll
+    for (int i = 0; i < kDma; ++i) {
+      const int r = wave * 64 + 8 * i + (lane >> 3);
+      vo[i] = (uint32_t)r * row_bytes + (uint32_t)(swz(r, lane & 7) << 4);
+    }
+    wave_off = (uint32_t)wave * (64 * kRowB);
+  }
+
+  // Stages 0..kPX-1 of B and 0..kPW-1 of A, issued in the same order the steady state uses
+  // (A first, then B, per virtual iteration).
+  __device__ __forceinline__ void prologue() {
+#pragma unroll
+    for (int vi = -kPX; vi < 0; ++vi) {
+      if (vi + kPW >= 0)
+        dma_rows<AUX_A>(ar, none, sl.w((vi + kPW) % kNW) + wave_off, vo, (uint32_t)(vi + kPW) * kRowB, vi + kPW < nkb);
+      dma_rows<AUX_B>(br, none, sl.x((vi + kPX) % kNX) + wave_off, vo, (uint32_t)(vi + kPX) * kRowB, vi + kPX < nkb);
+    }
+  }
+
+  // acc <- the product over all nkb stages (after prologue()).  On return every DMA has landed
+  // and every wave is past its last operand read (the slots may be reused).
+  __device__ __forceinline__ void run(f32x16 (&acc)[kMB][kNB], int wave, int lane) {
+    const int h = lane >> 5;
+    const int l32 = lane & 31;
+    // Operand reads: row r = l32 (+32 per block), chunk 2s + h of the 128-byte row segment.
+    uint32_t fo[kKSteps];
+#pragma unroll
+    for (int s = 0; s < kKSteps; ++s) fo[s] = (uint32_t)l32 * kRowB + (uint32_t)(swz(l32, 2 * s + h) << 4);
+    const uint32_t xo = (uint32_t)wave * (kRowsWave * kRowB);
+
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
+
+    // nkb >= 1 always: a do-while tells the compiler so, and spares it a second, never-run copy
+    // of the 256 zero accumulators held across the loop.
+    int j0 = 0;
+    do {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int j = j0 + u;
+        if (j >= nkb) break;
+        // Own DMAs of stage j are done; after the barrier everyone's are, and every wave has
+        // finished reading stage j - 1, whose slots the DMAs below overwrite.
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kVmBudget) & ~(15 << 8));  // and lgkmcnt(0)
+        bare_barrier();
+        // A DMAs at the head of the stage (they must precede this stage's B DMAs for the vmcnt
+        // budget); the B DMAs are spread over the MFMA stream below, so that a DMA waiting for
+        // room in the vector memory pipeline only delays MFMAs already queued.
+        dma_rows<AUX_A>(ar, none, sl.w((u + kPW) % kNW) + wave_off, vo, (uint32_t)(j + kPW) * kRowB, j + kPW < nkb);
+        __builtin_amdgcn_sched_barrier(0);
+        dma_rows<AUX_B>(br, none, sl.x((u + kPX) % kNX) + wave_off, vo, (uint32_t)(j + kPX) * kRowB, j + kPX < nkb);
+        const unsigned char* ws = sl.w(u % kNW);
+        const unsigned char* xsb = sl.x(u % kNX) + xo;
+        // Operand fragments are double-buffered: the 10 LDS reads of k-step s + 1 go out before
+        // the 16 MFMAs of k-step s, so their latency hides behind 512 MFMA cycles (one wave per
+        // SIMD has no other wave to hide it).
+        bf16x8 a[2][kMB], b[2][kNB];
+        auto fetch = [&](int buf, int s) {
+#pragma unroll
+          for (int nb = 0; nb < kNB; ++nb)
+            b[buf][nb] = *reinterpret_cast<const bf16x8*>(xsb + fo[s] + nb * (32 * kRowB));
+#pragma unroll
+          for (int mb = 0; mb < kMB; ++mb)
+            a[buf][mb] = *reinterpret_cast<const bf16x8*>(ws + fo[s] + mb * (32 * kRowB));
+        };
+        fetch(0, 0);
+        fetch(1, 1);
+#pragma unroll
+        for (int s = 0; s < kKSteps; ++s) {
+          if (s >= 1 && s + 1 < kKSteps) fetch((s + 1) & 1, s + 1);
+#pragma unroll
+          for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < kNB; ++nb)
+              acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][mb], b[s & 1][nb], acc[mb][nb], 0, 0, 0);
+        }
+        // Issue order for the scheduler: reads of steps 0 and 1; then per step its MFMAs with
+        // kDma / kKSteps B DMAs slotted between them, and the reads of step s + 2.
+        static_assert(kDma % kKSteps == 0 && (kMB * kNB) % (kDma / kKSteps) == 0, "DMA interleave");
+        constexpr int kDmaPerStep = kDma / kKSteps;
+        constexpr int kMfmaPerDma = kMB * kNB / kDmaPerStep;
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (kMB + kNB), 0);  // DS reads, steps 0 and 1
+#pragma unroll
+        for (int s = 0; s < kKSteps; ++s) {
+#pragma unroll
+          for (int q = 0; q < kDmaPerStep; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerDma, 0);  // MFMAs, step s
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);            // one B DMA
+          }
+          if (s + 2 < kKSteps) __builtin_amdgcn_sched_group_barrier(0x100, kMB + kNB, 0);  // DS reads, step s + 2
+        }
+      }
+      j0 += kUnroll;
+    } while (j0 < nkb);
+
+    // Drain the trailing dummy DMAs (they write slots the caller may reuse) and let every wave
+    // finish its last operand reads.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0) & ~(15 << 8));
+    bare_barrier();
+  }
+};
+
+}  // namespace tile
+}  // namespace elb

@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define ELB_VERSION 10200 /* major * 10000 + minor * 100 + patch */
+#define ELB_VERSION 10300 /* major * 10000 + minor * 100 + patch */
 
 typedef struct ihipStream_t* elb_stream_t; /* hipStream_t; NULL = default stream */
 
@@ -249,6 +249,32 @@ elb_status elb_permute_rows(const void* x, int32_t dtype, int64_t T, int32_t d, 
 elb_status elb_unpermute_combine(const void* expert_out, int32_t dtype, int64_t T, int32_t d, int32_t k,
                                  const int32_t* inv_perm, const float* gates, void* y, int32_t y_dtype,
                                  elb_stream_t stream);
+
+/*
+ * Router backward: gradients of
+ *   L = sum_{t,j} dgates[t,j] * gates[t,j] + zloss_coef * mean_t lse_t^2
+ * with respect to the tokens and the router weights, at the forward's selection topk_idx (the
+ * bias gets no gradient: it only acts inside Top-K).  The pages give no backward; this is the
+ * chain rule through the forward above (gates normalised over the K chosen unless
+ * ELB_GATES_RAW; the z-loss of the talk summary "Arcee Halts 400B Blackwell Model Collapse...",
+ * section "Precision Fallbacks, Loss Stabilization, and MaxVio ..."):
+ *   dL/dz_{t,i_j} = dL/ds_j s_j (1 - s_j),  dL/ds_j = (G_j - sum_m G_m g_m) / S (raw: G_j),
+ *   dL/dz_{t,i}  += (2 zloss_coef / T) lse_t softmax(z_t)_i,
+ *   dx = dL/dZ W [T, d] fp32,  dw = dL/dZ^T X [n_experts, d] fp32 (either may be NULL).
+ * The logits are recomputed from x and w on the matrix cores; dL/dz is rounded to bf16 before
+ * the two products, which accumulate in fp32.
+ *   x, w, topk_idx as in elb_router_forward (bf16 only, d % 64 == 0); dgates [T, k] fp32.
+ *   workspace: at least elb_backward_workspace_bytes(T, d, n_experts) bytes, 256-byte aligned;
+ *   contents on entry do not matter.  topk_idx entries must lie in [0, n_experts).
+ * Supported: 0 <= T <= 2^22, T * k < 2^31, 1 <= k <= min(8, n_experts), n_experts <= 256.
+ * Errors: ELB_ERR_NULL, ELB_ERR_SHAPE, ELB_ERR_UNSUPPORTED (dtype, d % 64, flag), ELB_ERR_ALIGN,
+ * ELB_ERR_WORKSPACE, ELB_ERR_LAUNCH.
+ */
+size_t elb_backward_workspace_bytes(int64_t T, int32_t d, int32_t n_experts);
+elb_status elb_router_backward(const void* x, int32_t dtype, int64_t T, int32_t d, const void* w, int32_t n_experts,
+                               int32_t k, uint32_t flags, const int32_t* topk_idx, const float* dgates,
+                               float zloss_coef, float* dx, float* dw, void* workspace, size_t workspace_bytes,
+                               elb_stream_t stream);
 
 /*
  * MaxVio of one step's loads: out[0] = max n / min n (the talk's definition, section

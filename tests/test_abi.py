@@ -225,3 +225,33 @@ def test_unpermute_combine_rejects(lib, kw, want):
 def test_route_step_zloss_needs_lse(lib):
     a = step_args(zloss=FAKE, lse=None)
     assert lib.elb_route_step(ctypes.byref(a), None) == NULL
+
+
+def test_backward_workspace_size(lib):
+    # dz^T + dz (256 x T_pad bf16 each), W^T (d x 256 bf16), X^T (d x T_pad bf16), dW partials
+    # (splits x 256 x d fp32), each rounded up to 256 bytes.  T_pad = 65536: 32 chunks of 2048.
+    T_pad, d = 65536, 3072
+    want = 2 * 256 * T_pad * 2 + d * 256 * 2 + d * T_pad * 2 + 32 * 256 * d * 4
+    assert lib.elb_backward_workspace_bytes(65536, 3072, 256) == want
+    # 2100 tokens -> T_pad 2304 = 9 tiles -> chunks of 3 tiles (768 tokens), 3 partials.
+    assert lib.elb_backward_workspace_bytes(2100, 192, 64) == 2 * 256 * 2304 * 2 + 192 * 256 * 2 + 192 * 2304 * 2 + \
+        3 * 256 * 192 * 4
+    assert lib.elb_backward_workspace_bytes(-1, 64, 8) == 0
+    assert lib.elb_backward_workspace_bytes(100, 100, 8) == 0
+    assert lib.elb_backward_workspace_bytes(100, 64, 300) == 0
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(w=None), NULL), (dict(ws=None), NULL), (dict(x=None), NULL), (dict(idx=None), NULL), (dict(g=None), NULL),
+    (dict(dtype=0), UNSUPPORTED), (dict(flags=2), UNSUPPORTED), (dict(d=96), UNSUPPORTED),
+    (dict(T=-1), SHAPE), (dict(T=(1 << 22) + 1), SHAPE), (dict(n=0), SHAPE), (dict(n=257), SHAPE), (dict(k=9), SHAPE),
+    (dict(n=4, k=5), SHAPE), (dict(zc=float("nan")), SHAPE), (dict(zc=float("inf")), SHAPE),
+    (dict(x=FAKE + 8), ALIGN), (dict(dw=FAKE + 4), ALIGN), (dict(ws=FAKE + 64), ALIGN), (dict(ws_bytes=1024), WORKSPACE),
+])
+def test_router_backward_rejects(lib, kw, want):
+    a = dict(x=FAKE, dtype=1, T=4096, d=256, w=FAKE, n=256, k=4, flags=0, idx=FAKE, g=FAKE, zc=0.0, dx=FAKE, dw=FAKE,
+             ws=FAKE, ws_bytes=1 << 40)
+    a.update(kw)
+    st = lib.elb_router_backward(a["x"], a["dtype"], a["T"], a["d"], a["w"], a["n"], a["k"], a["flags"], a["idx"],
+                                 a["g"], a["zc"], a["dx"], a["dw"], a["ws"], a["ws_bytes"], None)
+    assert st == want

@@ -29,7 +29,8 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, AMD published
 METRIC = "routed tokens/s (logits+top-4+counts+SMEBU) at N_r=256,K=4; % roofline"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "router_mfma_traffic.json")
-KERNEL_SOURCES = ["expert_load_balancing_amd/csrc/router_mfma.hip", "expert_load_balancing_amd/csrc/device_common.hpp"]
+KERNEL_SOURCES = ["expert_load_balancing_amd/csrc/router_mfma.hip", "expert_load_balancing_amd/csrc/mfma_tile.hpp",
+                  "expert_load_balancing_amd/csrc/device_common.hpp"]
 
 
 def kernel_source_hash() -> str:

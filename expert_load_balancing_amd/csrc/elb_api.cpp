@@ -207,7 +207,7 @@ elb_status elb_router_backward(const void* x, int32_t dtype, int64_t T, int32_t 
   if (T * (int64_t)k >= (int64_t(1) << 31) || d < 1 || (int64_t)d * 2 * 256 >= (int64_t(1) << 30)) return ELB_ERR_SHAPE;
   if (d % 64 != 0) return ELB_ERR_UNSUPPORTED;
   if (!(zloss_coef == zloss_coef) || zloss_coef - zloss_coef != 0.0f) return ELB_ERR_SHAPE;  // NaN or infinite
-  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(topk_idx, 4) || !aligned(dgates, 4) || !aligned(dx, 4) ||
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(topk_idx, 4) || !aligned(dgates, 4) || !aligned(dx, 16) ||
       !aligned(dw, 16) || !aligned(workspace, 256))
     return ELB_ERR_ALIGN;
   const elb::BackwardPlan plan = elb::backward_plan(T, d, workspace);

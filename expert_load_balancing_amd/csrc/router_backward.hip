@@ -235,17 +235,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   st.prologue();
   f32x16 acc[kMB][kNB];
   st.run(acc, wave, lane);
+  // Store the tile through the wave's own (now free) LDS slot, one 32-column block at a time:
+  // [256 rows][32 columns] fp32 = 32 KiB, then 16-byte pieces, 8 rows x 128 bytes per store.
   float* const Cz = C + (int64_t)blockIdx.z * c_split;
+  float* const stage = reinterpret_cast<float*>(wave == 0 ? xs0 : wave == 1 ? xs1 : wave == 2 ? xs2 : ws0);
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
-    const int64_t n = n0 + wave * kRowsWave + nb * 32 + l32;
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (m < c_rows && n < c_cols) Cz[m * ldc + n] = acc[mb][nb][r];
-      }
+      for (int r = 0; r < 16; ++r) stage[(mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) * 32 + l32] = acc[mb][nb][r];
+    wave_lds_sync();
+    const int64_t n = n0 + wave * kRowsWave + nb * 32 + (lane & 7) * 4;  // c_cols % 4 == 0: n..n+3 together
+#pragma unroll 8
+    for (int q = 0; q < 32; ++q) {
+      const int row = 8 * q + (lane >> 3);
+      const int64_t m = m0 + row;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(stage + row * 32 + (lane & 7) * 4);
+      if (m < c_rows && n < c_cols) *reinterpret_cast<f32x4*>(Cz + m * ldc + n) = v;
+    }
+    wave_lds_sync();  // the stage is read before the next block overwrites it
   }
 }
 

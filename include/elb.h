@@ -263,7 +263,8 @@ elb_status elb_unpermute_combine(const void* expert_out, int32_t dtype, int64_t 
  *   dx = dL/dZ W [T, d] fp32,  dw = dL/dZ^T X [n_experts, d] fp32 (either may be NULL).
  * The logits are recomputed from x and w on the matrix cores; dL/dz is rounded to bf16 before
  * the two products, which accumulate in fp32.
- *   x, w, topk_idx as in elb_router_forward (bf16 only, d % 64 == 0); dgates [T, k] fp32.
+ *   x, w, topk_idx as in elb_router_forward (bf16 only, d % 64 == 0); dgates [T, k] fp32;
+ *   dx and dw 16-byte aligned.
  *   workspace: at least elb_backward_workspace_bytes(T, d, n_experts) bytes, 256-byte aligned;
  *   contents on entry do not matter.  topk_idx entries must lie in [0, n_experts).
  * Supported: 0 <= T <= 2^22, T * k < 2^31, 1 <= k <= min(8, n_experts), n_experts <= 256.

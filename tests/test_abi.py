@@ -246,7 +246,8 @@ def test_backward_workspace_size(lib):
     (dict(dtype=0), UNSUPPORTED), (dict(flags=2), UNSUPPORTED), (dict(d=96), UNSUPPORTED),
     (dict(T=-1), SHAPE), (dict(T=(1 << 22) + 1), SHAPE), (dict(n=0), SHAPE), (dict(n=257), SHAPE), (dict(k=9), SHAPE),
     (dict(n=4, k=5), SHAPE), (dict(zc=float("nan")), SHAPE), (dict(zc=float("inf")), SHAPE),
-    (dict(x=FAKE + 8), ALIGN), (dict(dw=FAKE + 4), ALIGN), (dict(ws=FAKE + 64), ALIGN), (dict(ws_bytes=1024), WORKSPACE),
+    (dict(x=FAKE + 8), ALIGN), (dict(dw=FAKE + 4), ALIGN), (dict(dx=FAKE + 8), ALIGN), (dict(ws=FAKE + 64), ALIGN),
+    (dict(ws_bytes=1024), WORKSPACE),
 ])
 def test_router_backward_rejects(lib, kw, want):
     a = dict(x=FAKE, dtype=1, T=4096, d=256, w=FAKE, n=256, k=4, flags=0, idx=FAKE, g=FAKE, zc=0.0, dx=FAKE, dw=FAKE,

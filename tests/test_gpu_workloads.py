@@ -55,3 +55,33 @@ def test_full_size_workload(key):
     err = check_balance(wl.mode, counts64, b0, m0, bd.cpu().numpy(), md.cpu().numpy(), wl, delta.cpu().numpy())
     check_maxvio(mv.cpu().numpy(), counts64)
     log(f"  MaxVio {mv.cpu().numpy()[0]:.3f}, b/m error {err:.2e}")
+
+
+@pytest.mark.parametrize("key", ["tiny", "sign", "large", "stress"])
+def test_full_size_workload_fused_step(key):
+    """The same workloads through elb_route_step (one call, three or four kernels): outputs equal
+    the separate calls' bit for bit -- the generic kernel plus a counting pass for the fp32
+    workload, the dispatch scan over 1024 tiles for the stress workload."""
+    wl = datagen.WORKLOADS[key]
+    log(f"fused step on {wl.label}")
+    x, w = datagen.tokens(wl), datagen.router_weight(wl)
+    b0, m0 = datagen.initial_bias(wl), datagen.initial_momentum(wl)
+    xd, wd = to_dev(x), to_dev(w)
+    kw = dict(mode=wl.mode, lam=wl.lam, beta=wl.beta, kappa=wl.kappa, gamma=wl.gamma)
+    bs, ms = to_dev(b0), to_dev(m0)
+    cs = torch.zeros(wl.n_experts, dtype=torch.int32, device="cuda")
+    idx, gates, _ = elb.router_forward(xd, wd, bs, wl.k, counts=cs, accumulate=True)
+    offs, perm, inv = elb.router_dispatch(idx, wl.n_experts)
+    counts_sep = cs.clone()
+    delta, mv = elb.smebu_update(cs, bs, ms, want_delta=True, clear_counts=True, **kw)
+    bf, mf = to_dev(b0), to_dev(m0)
+    out = elb.RouterStep(wd, bf, mf, wl.k, wl.T, want_delta=True, **kw)(xd)
+    torch.cuda.synchronize()
+    pairs = [(out.topk_idx, idx), (out.gates, gates), (out.offsets, offs), (out.perm, perm), (out.inv_perm, inv),
+             (bf, bs), (mf, ms), (out.delta_b, delta), (out.maxvio, mv)]
+    for got, want in pairs:
+        assert np.array_equal(got.cpu().numpy(), want.cpu().numpy(), equal_nan=True)
+    assert (out.counts.cpu().numpy() == 0).all()
+    check_dispatch(offs.cpu().numpy(), perm.cpu().numpy(), inv.cpu().numpy(), idx.cpu().numpy(), wl.n_experts)
+    check_balance(wl.mode, counts_sep.cpu().numpy().astype(np.int64), b0, m0, bf.cpu().numpy(), mf.cpu().numpy(), wl,
+                  out.delta_b.cpu().numpy())

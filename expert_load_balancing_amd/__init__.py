@@ -362,7 +362,8 @@ class RouterStep:
         self._timing = None
 
     def set_timing(self, start: torch.cuda.Event | None, stop: torch.cuda.Event | None = None) -> None:
-        """Record ``start``/``stop`` (timing-enabled torch events) around the router kernel of later calls."""
+        """Record ``start``/``stop`` (timing-enabled torch events) around the router kernel of later
+        calls; ``set_timing(None)`` stops recording."""
         if start is None:
             self._timing, self._args.timing = None, None
             return

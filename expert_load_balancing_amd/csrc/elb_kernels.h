@@ -98,13 +98,10 @@ struct BackwardArgs {
   float* dw;  // [n_experts][d] fp32, or NULL
 };
 struct BackwardPlan {
-  int64_t T_pad;    // T rounded up to the 256-token tile (at least one tile)
-  int64_t k_chunk;  // tokens per dW partial
-  int splits;       // number of dW partials
-  uint16_t* dzt;    // dL/dz, expert-major [256][T_pad] bf16
-  uint16_t* dz;     // dL/dz, token-major [T_pad][256] bf16
-  uint16_t* wt;     // W^T [d][256] bf16
-  uint16_t* xt;     // X^T [d][T_pad] bf16
+  int64_t Q;        // 64-token stages of the batch
+  int n_col;        // 256-column tiles of d
+  int splits;       // token ranges of dW (one fp32 partial each)
+  uint16_t* dz;     // dL/dz, token-major [T][256] bf16
   float* part;      // dW partials [splits][256][d] fp32
   size_t bytes;     // workspace bytes
 };

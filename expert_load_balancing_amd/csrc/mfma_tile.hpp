@@ -1,8 +1,11 @@
 // One workgroup's 256 x 256 fp32 product tile on CDNA4 matrix cores (gfx950):
-//   acc[m][n] = sum_k A[m][k] * B[n][k]        m, n < 256; A, B bf16, rows contiguous in k
+//   acc[m][n] = sum_k A[m][k] * B[n][k]        m, n < 256; A, B bf16
 // held in registers, with both operands streamed from memory into LDS by buffer-to-LDS DMA.
-// The router forward uses it with A = the router weights and B = a tile of tokens (the logits,
-// transposed: Z^T = W X^T); the router backward uses it for its two weight-side products.
+// Each operand comes in one of two layouts (the policies RowsK and KRows below): rows
+// contiguous in k (row-major A[m][k]), or k-major (row-major A^T[k][m], read back transposed
+// by gfx950's transposing LDS read).  The router forward uses it with A = the router weights
+// and B = a tile of tokens, both rows contiguous in k (the logits, transposed: Z^T = W X^T);
+// the router backward's dW = dZ^T X contracts over tokens with both operands k-major.
 //
 // Work decomposition: 4 waves, one per SIMD; wave w owns B rows 64 w .. 64 w + 63 against all
 // 256 A rows, i.e. 8 x 2 accumulators of 32 x 32 (256 AGPRs).  A 32 x 32 MFMA output puts one
@@ -19,8 +22,8 @@
 //   waves and frees the slot the next DMA overwrites.  Barriers carry no memory fence: a fence
 //   on LDS would wait for every DMA in flight and drain the prefetch.  Near the end, dummy DMAs
 //   through an empty-range descriptor keep the vmcnt budget uniform; they move no bytes.  Within
-//   a slot, the eight 16-byte chunks of row r sit at chunk ^ ((r >> 1) & 7), which keeps the
-//   MFMA operand reads (16 rows x 16 bytes per LDS cycle over 64 banks) free of bank conflicts.
+//   a slot, 16-byte chunks are XOR-swizzled per row (see the layouts), which keeps the MFMA
+//   operand reads free of LDS bank conflicts.
 #pragma once
 
 #include "device_common.hpp"
@@ -111,33 +114,122 @@ struct Slots {
   __device__ __forceinline__ unsigned char* w(int i) const { return i == 0 ? w0 : w1; }
 };
 
-// The streaming product.  AUX_A / AUX_B: cache policies of the two streams.  Both operands'
-// rows are `row_bytes` apart; `nkb` stages of kBK elements are contracted (nkb >= 1).
-template <int AUX_A, int AUX_B>
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Operand layout: rows contiguous in k.  A slot holds 256 operand rows x 64 k (128 bytes); the
+// eight 16-byte chunks of row r sit at chunk ^ ((r >> 1) & 7).  A fragment (32 rows x 16 k) is
+// one 16-byte read per lane: row l % 32, k 8 (l / 32) .. + 7.
+struct RowsK {
+  static constexpr int kReads = 1;  // LDS reads per fragment
+  // DMA: instruction i of wave `wave` fills rows 64 wave + 8 i + lane / 8; lane position
+  // p = lane & 7 in the row receives the global chunk stored there, swz(row, p) (the swizzle is
+  // its own inverse).  One stage advances 128 bytes along every row.
+  __device__ static __forceinline__ uint32_t dma_off(int wave, int lane, int i, uint32_t row_bytes) {
+    const int r = wave * 64 + 8 * i + (lane >> 3);
+    return (uint32_t)r * row_bytes + (uint32_t)(swz(r, lane & 7) << 4);
+  }
+  __device__ static __forceinline__ uint32_t stage_bytes(uint32_t) { return kRowB; }
+  struct Lane {
+    uint32_t fo[kKSteps];
+    __device__ __forceinline__ void init(int lane) {
+#pragma unroll
+      for (int s = 0; s < kKSteps; ++s)
+        fo[s] = (uint32_t)(lane & 31) * kRowB + (uint32_t)(swz(lane & 31, 2 * s + (lane >> 5)) << 4);
+    }
+    // Block `blk` (rows 32 blk .. + 31) at k-step s.
+    __device__ __forceinline__ bf16x8 frag(const unsigned char* slot, int blk, int s) const {
+      return *reinterpret_cast<const bf16x8*>(slot + fo[s] + blk * (32 * kRowB));
+    }
+  };
+};
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes, lane 4 p + q
+// receives element q of the 8-byte pieces addressed by lanes p, p + 4, p + 8, p + 12 (in that
+// order).  So if lane 16 b + 4 j + p addresses k row (R + j) at columns C + 4 p .. + 3, lane
+// 16 b + 4 p + q receives column C + 4 p + q at k rows R .. R + 3.
+__device__ __forceinline__ i16x4 ds_read_tr16(const unsigned char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(const_cast<unsigned char*>(p)));
+}
+
+__device__ __forceinline__ bf16x8 join_tr(i16x4 lo, i16x4 hi) {
+  const __attribute__((ext_vector_type(8))) short v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Per-lane constants of a transposed fragment read.  A fragment's lane l (half hh = l / 32)
+// holds column l % 32 of its block and, as element i, k row 8 (i / 4) + 4 hh + (i & 3) of the
+// 16-row k-step (any fixed assignment of k is valid as long as both operands of a product use
+// it).  Reading it takes two transposed reads, elements 0..3 then 4..7: lane 16 b + 4 j + p
+// addresses k row 4 (b / 2) + j (+ 8 for the second read), columns 16 (b & 1) + 4 p .. + 3.
+struct TrLane {
+  uint32_t row;  // 4 (b / 2) + j
+  uint32_t col;  // byte offset of the lane's 8-byte piece inside its 64-byte block segment
+  uint32_t j;
+  __device__ __forceinline__ void init(int lane) {
+    const int b = lane >> 4, j_ = (lane >> 2) & 3, p = lane & 3;
+    row = (uint32_t)(4 * (b >> 1) + j_);
+    col = (uint32_t)(32 * (b & 1) + 8 * p);
+    j = (uint32_t)j_;
+  }
+};
+
+// Operand layout: k-major.  A slot holds 64 k rows x 256 operand columns (512 bytes); the 32
+// chunks of k row r sit at chunk ^ ((r & 3) << 2).  A transposed read then has each group of
+// 32 lanes read 4 consecutive k rows x 64 bytes, which the swizzle spreads over all 64 banks.
+struct KRows {
+  static constexpr int kReads = 2;
+  // DMA: instruction i of wave `wave` fills k rows 16 wave + 2 i + lane / 32, lane position
+  // p = lane & 31 receiving global chunk p ^ ((r & 3) << 2).  One stage advances 64 k rows.
+  __device__ static __forceinline__ uint32_t dma_off(int wave, int lane, int i, uint32_t row_bytes) {
+    const int r = wave * 16 + 2 * i + (lane >> 5);
+    return (uint32_t)r * row_bytes + (uint32_t)(((lane & 31) ^ ((r & 3) << 2)) << 4);
+  }
+  __device__ static __forceinline__ uint32_t stage_bytes(uint32_t row_bytes) { return 64u * row_bytes; }
+  struct Lane {
+    uint32_t base;  // k row offset + in-segment byte offset
+    uint32_t j;
+    __device__ __forceinline__ void init(int lane) {
+      TrLane t;
+      t.init(lane);
+      base = t.row * 512u + t.col;
+      j = t.j;  // = k row & 3: the swizzle moves block segment blk to blk ^ j
+    }
+    __device__ __forceinline__ bf16x8 frag(const unsigned char* slot, int blk, int s) const {
+      const unsigned char* p = slot + s * (16 * 512) + base + ((((uint32_t)blk) ^ j) << 6);
+      return join_tr(ds_read_tr16(p), ds_read_tr16(p + 8 * 512));
+    }
+  };
+};
+
+// The streaming product.  AUX_A / AUX_B: cache policies of the two streams; LA / LB: their
+// layouts.  A's rows are `a_row_bytes` apart, B's `b_row_bytes`; `nkb` stages of kBK elements
+// are contracted (nkb >= 1).
+template <int AUX_A, int AUX_B, class LA = RowsK, class LB = RowsK>
 struct Stream {
   __amdgpu_buffer_rsrc_t ar, br, none;
-  uint32_t vo[kDma];
-  uint32_t wave_off;
+  uint32_t voa[kDma], vob[kDma];
+  uint32_t wave_off, a_stage, b_stage;
   int nkb;
   Slots sl;
 
   // a_bytes / b_bytes: the readable bytes of each operand from its base (rows past them read 0).
-  __device__ __forceinline__ void init(const void* a, uint32_t a_bytes, const void* b, uint32_t b_bytes,
-                                       uint32_t row_bytes, int n_stages, int wave, int lane, Slots slots) {
+  __device__ __forceinline__ void init(const void* a, uint32_t a_bytes, uint32_t a_row_bytes, const void* b,
+                                       uint32_t b_bytes, uint32_t b_row_bytes, int n_stages, int wave, int lane,
+                                       Slots slots) {
     ar = make_rsrc(a, a_bytes);
     br = make_rsrc(b, b_bytes);
     none = make_rsrc(a, 0u);
     nkb = n_stages;
     sl = slots;
-    // DMA lane mapping: instruction i of wave `wave` fills rows wave*64 + 8 i + lane/8; lane
-    // position p = lane & 7 in the row receives the global chunk stored there, swz(row, p)
-    // (the swizzle is its own inverse).
 #pragma unroll
     for (int i = 0; i < kDma; ++i) {
-      const int r = wave * 64 + 8 * i + (lane >> 3);
-      vo[i] = (uint32_t)r * row_bytes + (uint32_t)(swz(r, lane & 7) << 4);
+      voa[i] = LA::dma_off(wave, lane, i, a_row_bytes);
+      vob[i] = LB::dma_off(wave, lane, i, b_row_bytes);
     }
-    wave_off = (uint32_t)wave * (64 * kRowB);
+    wave_off = (uint32_t)wave * (64 * kRowB);  // 8 KiB: 64 rows x 128 B or 16 rows x 512 B
+    a_stage = LA::stage_bytes(a_row_bytes);
+    b_stage = LB::stage_bytes(b_row_bytes);
   }
 
   // Stages 0..kPX-1 of B and 0..kPW-1 of A, issued in the same order the steady state uses
@@ -146,21 +238,20 @@ struct Stream {
 #pragma unroll
     for (int vi = -kPX; vi < 0; ++vi) {
       if (vi + kPW >= 0)
-        dma_rows<AUX_A>(ar, none, sl.w((vi + kPW) % kNW) + wave_off, vo, (uint32_t)(vi + kPW) * kRowB, vi + kPW < nkb);
-      dma_rows<AUX_B>(br, none, sl.x((vi + kPX) % kNX) + wave_off, vo, (uint32_t)(vi + kPX) * kRowB, vi + kPX < nkb);
+        dma_rows<AUX_A>(ar, none, sl.w((vi + kPW) % kNW) + wave_off, voa, (uint32_t)(vi + kPW) * a_stage,
+                        vi + kPW < nkb);
+      dma_rows<AUX_B>(br, none, sl.x((vi + kPX) % kNX) + wave_off, vob, (uint32_t)(vi + kPX) * b_stage,
+                      vi + kPX < nkb);
     }
   }
 
   // acc <- the product over all nkb stages (after prologue()).  On return every DMA has landed
   // and every wave is past its last operand read (the slots may be reused).
   __device__ __forceinline__ void run(f32x16 (&acc)[kMB][kNB], int wave, int lane) {
-    const int h = lane >> 5;
-    const int l32 = lane & 31;
-    // Operand reads: row r = l32 (+32 per block), chunk 2s + h of the 128-byte row segment.
-    uint32_t fo[kKSteps];
-#pragma unroll
-    for (int s = 0; s < kKSteps; ++s) fo[s] = (uint32_t)l32 * kRowB + (uint32_t)(swz(l32, 2 * s + h) << 4);
-    const uint32_t xo = (uint32_t)wave * (kRowsWave * kRowB);
+    typename LA::Lane la;
+    typename LB::Lane lb;
+    la.init(lane);
+    lb.init(lane);
 
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb)
@@ -184,22 +275,22 @@ struct Stream {
         // A DMAs at the head of the stage (they must precede this stage's B DMAs for the vmcnt
         // budget); the B DMAs are spread over the MFMA stream below, so that a DMA waiting for
         // room in the vector memory pipeline only delays MFMAs already queued.
-        dma_rows<AUX_A>(ar, none, sl.w((u + kPW) % kNW) + wave_off, vo, (uint32_t)(j + kPW) * kRowB, j + kPW < nkb);
+        dma_rows<AUX_A>(ar, none, sl.w((u + kPW) % kNW) + wave_off, voa, (uint32_t)(j + kPW) * a_stage,
+                        j + kPW < nkb);
         __builtin_amdgcn_sched_barrier(0);
-        dma_rows<AUX_B>(br, none, sl.x((u + kPX) % kNX) + wave_off, vo, (uint32_t)(j + kPX) * kRowB, j + kPX < nkb);
+        dma_rows<AUX_B>(br, none, sl.x((u + kPX) % kNX) + wave_off, vob, (uint32_t)(j + kPX) * b_stage,
+                        j + kPX < nkb);
         const unsigned char* ws = sl.w(u % kNW);
-        const unsigned char* xsb = sl.x(u % kNX) + xo;
-        // Operand fragments are double-buffered: the 10 LDS reads of k-step s + 1 go out before
+        const unsigned char* xs = sl.x(u % kNX);
+        // Operand fragments are double-buffered: the LDS reads of k-step s + 1 go out before
         // the 16 MFMAs of k-step s, so their latency hides behind 512 MFMA cycles (one wave per
         // SIMD has no other wave to hide it).
         bf16x8 a[2][kMB], b[2][kNB];
         auto fetch = [&](int buf, int s) {
 #pragma unroll
-          for (int nb = 0; nb < kNB; ++nb)
-            b[buf][nb] = *reinterpret_cast<const bf16x8*>(xsb + fo[s] + nb * (32 * kRowB));
+          for (int nb = 0; nb < kNB; ++nb) b[buf][nb] = lb.frag(xs, wave * kNB + nb, s);
 #pragma unroll
-          for (int mb = 0; mb < kMB; ++mb)
-            a[buf][mb] = *reinterpret_cast<const bf16x8*>(ws + fo[s] + mb * (32 * kRowB));
+          for (int mb = 0; mb < kMB; ++mb) a[buf][mb] = la.frag(ws, mb, s);
         };
         fetch(0, 0);
         fetch(1, 1);
@@ -217,7 +308,8 @@ struct Stream {
         static_assert(kDma % kKSteps == 0 && (kMB * kNB) % (kDma / kKSteps) == 0, "DMA interleave");
         constexpr int kDmaPerStep = kDma / kKSteps;
         constexpr int kMfmaPerDma = kMB * kNB / kDmaPerStep;
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (kMB + kNB), 0);  // DS reads, steps 0 and 1
+        constexpr int kReadsStep = kMB * LA::kReads + kNB * LB::kReads;
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kReadsStep, 0);  // DS reads, steps 0 and 1
 #pragma unroll
         for (int s = 0; s < kKSteps; ++s) {
 #pragma unroll
@@ -225,7 +317,7 @@ struct Stream {
             __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerDma, 0);  // MFMAs, step s
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);            // one B DMA
           }
-          if (s + 2 < kKSteps) __builtin_amdgcn_sched_group_barrier(0x100, kMB + kNB, 0);  // DS reads, step s + 2
+          if (s + 2 < kKSteps) __builtin_amdgcn_sched_group_barrier(0x100, kReadsStep, 0);  // DS reads, step s + 2
         }
       }
       j0 += kUnroll;

@@ -14,16 +14,18 @@
 // section 2.3; the z-loss is the talk summary "Arcee Halts 400B Blackwell Model Collapse...",
 // section "Precision Fallbacks, Loss Stabilization, and MaxVio as Data Telemetry".
 //
-// Launches (all bf16 operands, fp32 accumulation):
-//  1. grad_logits: the forward's streaming product recomputes each 256-token tile of logits in
-//     registers; the epilogue forms dL/dz from the tile's logits, the forward's topk_idx and the
-//     upstream gate gradients, and stores it rounded to bf16 expert-major (dZ^T [256][T_pad]):
-//     a lane holds 32 consecutive tokens of one expert row per store.
-//  2. transposes (64 x 64 tiles through LDS): dZ^T -> dZ [T_pad][256], W -> W^T [d][256],
-//     X -> X^T [d][T_pad], zero-padded, so that both products below contract contiguous rows.
-//  3. dX = dZ W as the streaming product with A = dZ (256 tokens), B = W^T (256 columns of d).
-//  4. dW = dZ^T X as the streaming product with A = dZ^T (all experts), B = X^T (256 columns of
-//     d), split over token chunks into fp32 partials, then summed over the chunks in order.
+// Launches (all bf16 operands, fp32 accumulation; no transposed copies anywhere):
+//  1. grad_kernel, one workgroup per 256-token tile:
+//     a. the forward's streaming product recomputes the tile's logits in registers;
+//     b. the epilogue parks them in LDS, forms dL/dz for each token from them, the forward's
+//        topk_idx and the upstream gate gradients, rounds it to bf16 into MFMA operand
+//        fragments held in registers, and stores it token-major (dZ [T][256], for dW);
+//     c. dX = dZ W for the tile: W streams through LDS 64 columns at a time and is read back
+//        transposed (k = experts is W's row index), against the dZ fragments in registers; the
+//        fp32 result leaves through an LDS stage as whole 256-byte row segments.
+//  2. dw_kernel: dW = dZ^T X contracts over tokens with both operands k-major (dZ and X
+//     token-major, read back transposed), split over token ranges into fp32 partials.
+//  3. reduce_partials_kernel: dW = the partials summed in range order.
 // dL/dz is rounded to bf16 before the two products (the usual training precision); the fp32
 // accumulation and the rounding are the only departures from exact arithmetic.
 #include "../../include/elb.h"
@@ -37,23 +39,28 @@ namespace {
 using namespace tile;
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kCtas = 256;  // compute units: the dW split count aims at one workgroup per CU
 
-__device__ __forceinline__ uint16_t bf16_rne(float f) {
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
   // Round to nearest, ties to even (values are finite).
   const uint32_t u = __float_as_uint(f);
-  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
 __device__ __forceinline__ float sigmoid_fast(float z) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
 }
 
-// dZ^T [256][ld] (bf16) of one 256-token tile.  zc2 = 2 c / T (0: no z-loss term).
+constexpr int kDxStores = 16;  // stores per wave per dX stage: 64 tokens x 64 columns fp32, 1 KiB each
+constexpr int kDxAhead = 3;  // k-blocks of W fragments read ahead (4 reads each, <= 15 in flight)
+
+// One 256-token tile: dZ [t][256] (bf16, token-major; NULL: not stored) and dX [t][d] (fp32;
+// NULL: not computed).  zc2 = 2 c / T (0: no z-loss term).
 template <int K, bool FULL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void grad_logits_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void grad_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int64_t T, int d, int n_experts, int normalize,
-    const int32_t* __restrict__ idx, const float* __restrict__ dgates, float zc2, uint16_t* __restrict__ dzt,
-    int64_t ld) {
+    const int32_t* __restrict__ idx, const float* __restrict__ dgates, float zc2, uint16_t* __restrict__ dz,
+    float* __restrict__ dx) {
   __shared__ __attribute__((aligned(1024))) unsigned char xs0[kSlot], xs1[kSlot], xs2[kSlot];
   __shared__ __attribute__((aligned(1024))) unsigned char ws0[kSlot], ws1[kSlot];
   const int tid = threadIdx.x;
@@ -64,181 +71,270 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int64_t row0 = (int64_t)blockIdx.x * kRowsB;
   const int rows = (int)(T - row0 < kRowsB ? T - row0 : kRowsB);
   const uint32_t row_bytes = (uint32_t)d * 2u;
-  Stream<kAuxCached, kAuxStream> st;
-  st.init(w, (uint32_t)n_experts * row_bytes, x + row0 * d, (uint32_t)rows * row_bytes, row_bytes, d / kBK, wave,
-          lane, Slots{xs0, xs1, xs2, ws0, ws1});
-  st.prologue();
-  f32x16 acc[kMB][kNB];
-  st.run(acc, wave, lane);
 
-  // Each wave parks its scores in a slot of its own: [32 row groups][64 lanes][4 floats].
-  float* const park = reinterpret_cast<float*>(wave == 0 ? xs0 : wave == 1 ? xs1 : wave == 2 ? xs2 : ws0);
+  // fr[nb][kb]: the MFMA operand fragment of dL/dz for token block nb (tokens 32 nb + lane % 32
+  // of the wave's 64), k-block kb (experts 16 kb .. + 15): element i = expert
+  // 16 kb + 8 (i / 4) + 4 h + (i & 3), as bf16 pairs.
+  uint32_t fr[kNB][16][4];
+  {
+    // ---- a. logits of the tile: Z^T = W X^T, token columns per lane ----
+    Stream<kAuxCached, kAuxStream> st;
+    st.init(w, (uint32_t)n_experts * row_bytes, row_bytes, x + row0 * d, (uint32_t)rows * row_bytes, row_bytes,
+            d / kBK, wave, lane, Slots{xs0, xs1, xs2, ws0, ws1});
+    st.prologue();
+    f32x16 acc[kMB][kNB];
+    st.run(acc, wave, lane);
+
+    // Each wave parks its logits in a slot of its own, [32 groups][64 lanes][4 floats]: group
+    // q = 4 mb + g holds acc[mb][nb][4 g .. 4 g + 3], experts 32 mb + 8 g + 4 h + 0..3 of the
+    // lane's token.  Reading them back from LDS keeps the epilogue's registers free.
+    float* const park = reinterpret_cast<float*>(wave == 0 ? xs0 : wave == 1 ? xs1 : wave == 2 ? xs2 : ws0);
+    auto own = [&](int q) { return *reinterpret_cast<const f32x4*>(park + (q * 64 + lane) * 4); };
 #pragma unroll
-  for (int nb = 0; nb < kNB; ++nb) {
-    const int64_t t = row0 + wave * kRowsWave + nb * 32 + l32;
-    const bool live = t < T;
-    // log-sum-exp of the token's logits (the lane's 128, merged with lane ^ 32's).
-    float lse = 0.0f;
-    if (zc2 != 0.0f) {
-      float m = -__builtin_inff();
+    for (int nb = 0; nb < kNB; ++nb) {
 #pragma unroll
       for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int e = mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (FULL || e < n_experts) m = fmaxf(m, acc[mb][nb][r]);
+        for (int g = 0; g < 4; ++g) {
+          f32x4 v;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = acc[mb][nb][4 * g + r];
+          *reinterpret_cast<f32x4*>(park + ((mb * 4 + g) * 64 + lane) * 4) = v;
         }
-      float sum = 0.0f;
+      wave_lds_sync();
+      const int64_t t = row0 + wave * kRowsWave + nb * 32 + l32;
+      const bool live = t < T;
+
+      // ---- b. dL/dz ----
+      // log-sum-exp of the token's logits (the lane's 128, merged with lane ^ 32's).
+      float lse = 0.0f;
+      if (zc2 != 0.0f) {
+        float m = -__builtin_inff();
 #pragma unroll
-      for (int mb = 0; mb < kMB; ++mb)
+        for (int q = 0; q < 32; ++q) {
+          const f32x4 v = own(q);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int e = mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (FULL || e < n_experts) sum += __builtin_amdgcn_exp2f((acc[mb][nb][r] - m) * kLog2e);
+          for (int r = 0; r < 4; ++r)
+            if (FULL || (q >> 2) * 32 + 8 * (q & 3) + 4 * h + r < n_experts) m = fmaxf(m, v[r]);
         }
-      const float m2 = __shfl_xor(m, 32);
-      const float sum2 = __shfl_xor(sum, 32);
-      const float mm = fmaxf(m, m2);
-      lse = mm + __logf(sum * __builtin_amdgcn_exp2f((m - mm) * kLog2e) + sum2 * __builtin_amdgcn_exp2f((m2 - mm) * kLog2e));
+        float sum = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 32; ++q) {
+          const f32x4 v = own(q);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (FULL || (q >> 2) * 32 + 8 * (q & 3) + 4 * h + r < n_experts)
+              sum += __builtin_amdgcn_exp2f((v[r] - m) * kLog2e);
+        }
+        const float m2 = __shfl_xor(m, 32);
+        const float sum2 = __shfl_xor(sum, 32);
+        const float mm = fmaxf(m, m2);
+        lse = mm + __logf(sum * __builtin_amdgcn_exp2f((m - mm) * kLog2e) +
+                          sum2 * __builtin_amdgcn_exp2f((m2 - mm) * kLog2e));
+      }
+      // dL/dz at the K chosen experts: their logits come from either lane of the pair.
+      int e[K];
+      float dzs[K];
+      {
+        float s[K], G[K];
+        float S = 0.0f;
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+          e[j] = live ? idx[t * K + j] : -1;
+          G[j] = live ? dgates[t * K + j] : 0.0f;
+          const int ej = e[j] < 0 ? 0 : (e[j] > kRowsA - 1 ? kRowsA - 1 : e[j]);  // stay inside the park
+          s[j] = sigmoid_fast(park[((ej >> 3) * 64 + l32 + 32 * ((ej >> 2) & 1)) * 4 + (ej & 3)]);
+          S += s[j];
+        }
+        float Gg = 0.0f;
+        const float inv = 1.0f / S;
+        if (normalize) {
+#pragma unroll
+          for (int j = 0; j < K; ++j) Gg += G[j] * (s[j] * inv);
+        }
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+          const float ds = normalize ? (G[j] - Gg) * inv : G[j];
+          dzs[j] = ds * s[j] * (1.0f - s[j]);
+        }
+      }
+      // Every expert of the lane: z-loss part plus the chosen-expert part; padded experts and
+      // tokens past T get 0.  Rounded to bf16 into the fragments; stored token-major.
+      const float zl = zc2 * lse;
+      uint16_t* const drow = dz + (live ? t : 0) * kRowsA + 4 * h;
+#pragma unroll
+      for (int kb = 0; kb < 16; ++kb) {
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+          const f32x4 zv = own(2 * kb + qq);  // experts 16 kb + 8 qq + 4 h + 0..3
+          uint32_t b[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int ex = 16 * kb + 8 * qq + 4 * h + r;
+            float v = 0.0f;
+            if (zc2 != 0.0f) v = zl * __builtin_amdgcn_exp2f((zv[r] - lse) * kLog2e);
+#pragma unroll
+            for (int j = 0; j < K; ++j) v += e[j] == ex ? dzs[j] : 0.0f;
+            if (!live || (!FULL && ex >= n_experts)) v = 0.0f;
+            b[r] = bf16_rne(v);
+          }
+          fr[nb][kb][2 * qq] = b[0] | (b[1] << 16);
+          fr[nb][kb][2 * qq + 1] = b[2] | (b[3] << 16);
+        }
+        if (dz != nullptr && live) {
+          *reinterpret_cast<uint2*>(drow + 16 * kb) = uint2{fr[nb][kb][0], fr[nb][kb][1]};
+          *reinterpret_cast<uint2*>(drow + 16 * kb + 8) = uint2{fr[nb][kb][2], fr[nb][kb][3]};
+        }
+      }
+      wave_lds_sync();  // the park is read before the next block's logits overwrite it
     }
-    // Scores of the lane's experts, parked so that either lane of the pair can read any of them.
-#pragma unroll
-    for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 sv;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sv[r] = sigmoid_fast(acc[mb][nb][g * 4 + r]);
-        *reinterpret_cast<f32x4*>(park + ((mb * 4 + g) * 64 + lane) * 4) = sv;
-      }
-    wave_lds_sync();
-    // dL/dz at the K chosen experts.
-    int e[K];
-    float dzs[K];
-    {
-      float s[K], G[K];
-      float S = 0.0f;
-#pragma unroll
-      for (int j = 0; j < K; ++j) {
-        e[j] = live ? idx[t * K + j] : -1;
-        G[j] = live ? dgates[t * K + j] : 0.0f;
-        const int ej = e[j] < 0 ? 0 : (e[j] > kRowsA - 1 ? kRowsA - 1 : e[j]);  // stay inside the park
-        s[j] = park[((ej >> 3) * 64 + l32 + 32 * ((ej >> 2) & 1)) * 4 + (ej & 3)];
-        S += s[j];
-      }
-      float Gg = 0.0f;
-      const float inv = 1.0f / S;
-      if (normalize) {
-#pragma unroll
-        for (int j = 0; j < K; ++j) Gg += G[j] * (s[j] * inv);
-      }
-#pragma unroll
-      for (int j = 0; j < K; ++j) {
-        const float ds = normalize ? (G[j] - Gg) * inv : G[j];
-        dzs[j] = ds * s[j] * (1.0f - s[j]);
-      }
-    }
-    wave_lds_sync();  // every lane has read the park before it is overwritten below
-    // dL/dz for each of the lane's experts: z-loss part plus the chosen-expert part; padded
-    // experts and tokens past T get 0.  Staged as bf16 in the park, expert-major
-    // [256 experts][32 tokens], then written out in 16-byte pieces: 64 bytes per expert row.
-    uint16_t* const stage = reinterpret_cast<uint16_t*>(park);
-    const float zl = zc2 * lse;
-#pragma unroll
-    for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ex = mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        float v = 0.0f;
-        if (zc2 != 0.0f) v = zl * __builtin_amdgcn_exp2f((acc[mb][nb][r] - lse) * kLog2e);
-#pragma unroll
-        for (int j = 0; j < K; ++j) v += e[j] == ex ? dzs[j] : 0.0f;
-        if (!live || (!FULL && ex >= n_experts)) v = 0.0f;
-        stage[ex * 32 + l32] = bf16_rne(v);
-      }
-    wave_lds_sync();
-    // 256 rows x 4 pieces = 1024 pieces, 16 per lane: lane l takes piece q * 64 + l, i.e. row
-    // 16 q + l / 4, piece l % 4 (tokens 8 (l % 4) .. + 7 of this block).
-    const int64_t t0 = row0 + wave * kRowsWave + nb * 32;
-    uint16_t* const out = dzt + (int64_t)(lane >> 2) * ld + t0 + (lane & 3) * 8;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int row = 16 * q + (lane >> 2);
-      const uint4 v = *reinterpret_cast<const uint4*>(stage + row * 32 + (lane & 3) * 8);
-      *reinterpret_cast<uint4*>(out + (int64_t)(16 * q) * ld) = v;
-    }
-    wave_lds_sync();  // the stage is read before the next block's scores overwrite it
   }
+  if (dx == nullptr) return;
+
+  // ---- c. dX = dZ W for the tile's tokens ----
+  // Every wave is done with its park and every load and store above has completed, so the
+  // slots are free and the vmcnt budgets below start from zero.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0) & ~(15 << 8));
+  bare_barrier();
+  // W slots xs0 / xs1: 256 expert rows x 64 columns (128 bytes), rows past n_experts read 0.
+  // Chunks of row r sit at chunk ^ (((r >> 1) & 1) << 2): a transposed read has each group of
+  // 32 lanes read 4 consecutive rows (two per 256-byte bank window) x 64 bytes, and the swizzle
+  // puts rows r and r + 2 in different halves of their window.  Store stage: xs2, 8 KiB a wave.
+  //
+  // Ordering.  The compiler makes a transposed LDS read wait for every LDS DMA issued before it
+  // (the read carries no alias information), so stage j + 1's DMAs go out only after stage j's
+  // last read: one slot is read while the other fills.  Stage j then needs only its own DMAs,
+  // behind which come the 16 stores of stage j - 1: vmcnt(16) leaves those stores in flight.
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, (uint32_t)n_experts * row_bytes);
+  uint32_t vo[kDma];
+#pragma unroll
+  for (int i = 0; i < kDma; ++i) {
+    const int r = wave * 64 + 8 * i + (lane >> 3);
+    vo[i] = (uint32_t)r * row_bytes + (uint32_t)(((lane & 7) ^ (((r >> 1) & 1) << 2)) << 4);
+  }
+  const uint32_t wave_off = (uint32_t)wave * (64 * kRowB);
+  const int nst = d / kBK;
+  auto dma = [&](unsigned char* slot, int j) {
+    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)j * kRowB);  // scalar: see below
+#pragma unroll
+    for (int i = 0; i < kDma; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, ELB_AS3(slot + wave_off + i * 1024), 16, vo[i], (int)soff, 0,
+                                               kAuxCached);
+  };
+  dma(xs0, 0);
+  // Stores go through a descriptor covering the tile's live rows: rows past T are dropped while
+  // every store instruction still issues (the vmcnt budget counts them).  They are non-temporal:
+  // with normal allocation the dX stream would push W out of L2, where every CU re-reads it.
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(dx + row0 * d, (uint32_t)rows * (uint32_t)d * 4u);
+  TrLane tl;
+  tl.init(lane);
+  const uint32_t ro = tl.row * (uint32_t)kRowB + tl.col;
+  const uint32_t sw = ((tl.j >> 1) & 1u) << 6;  // ((row >> 1) & 1) << 2 chunks = 64 bytes
+  // Store q of a half: token rows wave*64 + 8 q + lane / 8, 16 bytes at column 4 (lane % 8).
+  const uint32_t so = (uint32_t)(wave * kRowsWave + (lane >> 3)) * (uint32_t)d * 4u + (uint32_t)(lane & 7) * 16u;
+  const uint32_t q_stride = 8u * (uint32_t)d * 4u;
+  unsigned char* const stg = xs2 + wave * (kSlot / 4);
+  // W fragment of k-block kb (experts 16 kb .. + 15), columns 32 cb .. + 31 of the stage.
+  auto frag = [&](const unsigned char* sl, int kb, int cb) {
+    const unsigned char* p = sl + kb * (16 * kRowB) + ro + (((uint32_t)cb << 6) ^ sw);
+    return join_tr(ds_read_tr16(p), ds_read_tr16(p + 8 * kRowB));
+  };
+  // Stage j: multiply the W columns in `cur`, start stage j + 1's DMAs into `nxt`, store.
+  auto stage = [&](int j, const unsigned char* cur, unsigned char* nxt) {
+    f32x16 c[2][kNB];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) c[cb][nb][r] = 0.0f;
+    // Fragments run kDxAhead k-blocks ahead of the MFMAs that use them: 4 MFMAs (128 cycles) per
+    // k-block do not cover an LDS read's latency while four waves share the LDS.
+    bf16x8 a[kDxAhead + 1][2];
+#pragma unroll
+    for (int kb = 0; kb < kDxAhead; ++kb) {
+      a[kb][0] = frag(cur, kb, 0);
+      a[kb][1] = frag(cur, kb, 1);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 16; ++kb) {
+      if (kb + kDxAhead < 16) {
+        a[(kb + kDxAhead) % (kDxAhead + 1)][0] = frag(cur, kb + kDxAhead, 0);
+        a[(kb + kDxAhead) % (kDxAhead + 1)][1] = frag(cur, kb + kDxAhead, 1);
+      }
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb) {
+          const i32x4 bv = {(int)fr[nb][kb][0], (int)fr[nb][kb][1], (int)fr[nb][kb][2], (int)fr[nb][kb][3]};
+          c[cb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb % (kDxAhead + 1)][cb],
+                                                             __builtin_bit_cast(bf16x8, bv), c[cb][nb], 0, 0, 0);
+        }
+    }
+    // Issue order: the reads of the first kDxAhead k-blocks; then per k-block the reads of the one
+    // kDxAhead further and its 4 MFMAs.
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 * kDxAhead, 0);
+#pragma unroll
+    for (int kb = 0; kb < 16; ++kb) {
+      if (kb + kDxAhead < 16) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (j + 1 < nst) dma(nxt, j + 1);
+    // Stores go out as whole 256-byte row segments, one 32-column half of the 64 x 64 fp32 tile
+    // at a time through the wave's LDS stage: [64 tokens][8 chunks of 16 bytes], chunk ch of
+    // token row t at ch ^ (t & 7).  Lane: token 32 nb + l32 of the wave; accumulator 4 g + r:
+    // column 32 cb + 8 g + 4 h + r of the stage, i.e. chunk 2 g + h of half cb.
+    const uint32_t ssoff = __builtin_amdgcn_readfirstlane((uint32_t)j * (kBK * 4));
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int t = nb * 32 + l32;
+          const f32x4 v = {c[cb][nb][4 * g], c[cb][nb][4 * g + 1], c[cb][nb][4 * g + 2], c[cb][nb][4 * g + 3]};
+          *reinterpret_cast<f32x4*>(stg + t * 128 + (((2 * g + h) ^ (t & 7)) << 4)) = v;
+        }
+      // Store q: tokens 8 q .. 8 q + 7, 8 lanes (8 chunks) per token row.
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int t = 8 * q + (lane >> 3);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(stg + t * 128 + (((lane & 7) ^ (t & 7)) << 4));
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), xr,
+                                               (int)(so + (uint32_t)q * q_stride + (uint32_t)cb * 128u), (int)ssoff,
+                                               kAuxStream);
+      }
+    }
+  };
+  // Stage 0 needs only its own DMAs; stage j >= 1 has the 16 stores of stage j - 1 behind them.
+  // (Offsets are forced wave-uniform with readfirstlane: a vector offset would turn every DMA and
+  // store into a loop over distinct lane values.)
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0) & ~(15 << 8));
+  bare_barrier();
+  stage(0, xs0, xs1);
+  for (int j = 1; j < nst; j += 2) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDxStores) & ~(15 << 8));
+    bare_barrier();
+    stage(j, xs1, xs0);
+    if (j + 1 >= nst) break;
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDxStores) & ~(15 << 8));
+    bare_barrier();
+    stage(j + 1, xs0, xs1);
+  }
+  // The stores drain before the workgroup ends.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0) & ~(15 << 8));
 }
 
-// out[c][r] = in[r][c] for r < R, 0 for R <= r < R_pad; c < C (C % 64 == 0).  64 x 64 tiles.
-__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ in, int64_t R, int64_t C,
-                                                             int64_t ldi, uint16_t* __restrict__ out, int64_t ldo) {
-  __shared__ uint16_t tile[64][64 + 2];
-  const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
-  const int tid = threadIdx.x;
-  // Load: 64 rows x 8 chunks of 8 elements; thread -> (row, chunk), two passes.
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int q = tid + 256 * p, rr = q >> 3, ch = q & 7;
-    const int64_t r = r0 + rr;
-    uint16_t v[8];
-    if (r < R) {
-      const uint4 u = *reinterpret_cast<const uint4*>(in + r * ldi + c0 + ch * 8);
-      const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[2 * i] = (uint16_t)(uw[i] & 0xFFFF);
-        v[2 * i + 1] = (uint16_t)(uw[i] >> 16);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = 0;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) tile[rr][ch * 8 + i] = v[i];
-  }
-  __syncthreads();
-  // Store: 64 output rows (c) x 8 chunks of 8 r values.
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int q = tid + 256 * p, cc = q >> 3, ch = q & 7;
-    uint32_t uw[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) uw[i] = (uint32_t)tile[ch * 8 + 2 * i][cc] | ((uint32_t)tile[ch * 8 + 2 * i + 1][cc] << 16);
-    *reinterpret_cast<uint4*>(out + (c0 + cc) * ldo + r0 + ch * 8) = uint4{uw[0], uw[1], uw[2], uw[3]};
-  }
-}
-
-// C[m][n] (+ z * c_split) = sum over k in chunk z of A[m][k] B[n][k]; A rows m < a_rows, B rows
-// n < b_rows (rows past them read 0), rows row_bytes apart; chunk z covers k in
-// [z * kc, (z + 1) * kc) (kc = k_stages * 64).  Stores m < c_rows, n < c_cols, row stride ldc.
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_nt_kernel(
-    const uint16_t* __restrict__ A, int64_t a_rows, const uint16_t* __restrict__ B, int64_t b_rows, int64_t ld,
-    int k_stages, float* __restrict__ C, int64_t c_rows, int64_t c_cols, int64_t ldc, int64_t c_split) {
-  __shared__ __attribute__((aligned(1024))) unsigned char xs0[kSlot], xs1[kSlot], xs2[kSlot];
-  __shared__ __attribute__((aligned(1024))) unsigned char ws0[kSlot], ws1[kSlot];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+// Store a 256 x 256 fp32 tile (acc of the streaming product, rows m of A, columns n of B)
+// through the wave's own LDS slot, one 32-column block at a time ([256 rows][32 columns] fp32 =
+// 32 KiB), then in 16-byte pieces, 8 rows x 128 bytes per store.  Stores m < c_rows, n < c_cols
+// (c_cols % 4 == 0), row stride ldc.
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[kMB][kNB], float* stage, float* C, int64_t ldc,
+                                           int64_t m0, int64_t n0, int64_t c_rows, int64_t c_cols, int wave,
+                                           int lane) {
   const int h = lane >> 5;
   const int l32 = lane & 31;
-  const int64_t m0 = (int64_t)blockIdx.x * kRowsA, n0 = (int64_t)blockIdx.y * kRowsB;
-  const int64_t k0 = (int64_t)blockIdx.z * k_stages * kBK;
-  const int64_t am = a_rows - m0 < kRowsA ? a_rows - m0 : kRowsA;
-  const int64_t bn = b_rows - n0 < kRowsB ? b_rows - n0 : kRowsB;
-  const uint32_t row_bytes = (uint32_t)(ld * 2);
-  const uint32_t span = (uint32_t)(k_stages * kRowB);  // bytes of one row in this chunk
-  Stream<kAuxStream, kAuxStream> st;
-  st.init(A + m0 * ld + k0, (uint32_t)((am - 1) * row_bytes + span), B + n0 * ld + k0,
-          (uint32_t)((bn - 1) * row_bytes + span), row_bytes, k_stages, wave, lane, Slots{xs0, xs1, xs2, ws0, ws1});
-  st.prologue();
-  f32x16 acc[kMB][kNB];
-  st.run(acc, wave, lane);
-  // Store the tile through the wave's own (now free) LDS slot, one 32-column block at a time:
-  // [256 rows][32 columns] fp32 = 32 KiB, then 16-byte pieces, 8 rows x 128 bytes per store.
-  float* const Cz = C + (int64_t)blockIdx.z * c_split;
-  float* const stage = reinterpret_cast<float*>(wave == 0 ? xs0 : wave == 1 ? xs1 : wave == 2 ? xs2 : ws0);
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
 #pragma unroll
@@ -246,24 +342,57 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
       for (int r = 0; r < 16; ++r) stage[(mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) * 32 + l32] = acc[mb][nb][r];
     wave_lds_sync();
-    const int64_t n = n0 + wave * kRowsWave + nb * 32 + (lane & 7) * 4;  // c_cols % 4 == 0: n..n+3 together
+    const int64_t n = n0 + wave * kRowsWave + nb * 32 + (lane & 7) * 4;
 #pragma unroll 8
     for (int q = 0; q < 32; ++q) {
       const int row = 8 * q + (lane >> 3);
       const int64_t m = m0 + row;
       const f32x4 v = *reinterpret_cast<const f32x4*>(stage + row * 32 + (lane & 7) * 4);
-      if (m < c_rows && n < c_cols) *reinterpret_cast<f32x4*>(Cz + m * ldc + n) = v;
+      if (m < c_rows && n < c_cols) *reinterpret_cast<f32x4*>(C + m * ldc + n) = v;
     }
     wave_lds_sync();  // the stage is read before the next block overwrites it
   }
 }
 
-// out[i] = sum_{s < S} part[s * stride + i], in order s = 0, 1, ...; n4 float4 elements.
+// part[z][m][n0 + n] = sum over tokens t of range z of dZ[t][m] X[t][n0 + n]   (m, n < 256).
+// Range z covers 64-token stages [Q z / S, Q (z + 1) / S) (Q = ceil(T / 64), S = splits).  The
+// workgroups that share a range run on one XCD (a linear id L runs on XCD L % 8), so its dZ rows
+// come from HBM once into that XCD's L2 and serve all n_col column tiles there.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void dw_kernel(
+    const uint16_t* __restrict__ dz, const uint16_t* __restrict__ x, int64_t T, int d, int64_t Q, int splits,
+    int n_col, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(1024))) unsigned char xs0[kSlot], xs1[kSlot], xs2[kSlot];
+  __shared__ __attribute__((aligned(1024))) unsigned char ws0[kSlot], ws1[kSlot];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // XCD-grouped order: XCD x holds G / 8 (+1 for x < G % 8) consecutive work items.
+  const int G = (int)gridDim.x;
+  const int L = (int)blockIdx.x;
+  const int xcd = L & 7, slot = L >> 3;
+  const int o = xcd * (G >> 3) + (xcd < (G & 7) ? xcd : (G & 7)) + slot;
+  const int z = o / n_col, col = o - z * n_col;
+  const int64_t s0 = Q * z / splits, s1 = Q * (z + 1) / splits;
+  const int64_t t0 = s0 * kBK;
+  const int64_t t1 = s1 * kBK < T ? s1 * kBK : T;
+  const int64_t n0 = (int64_t)col * kRowsB;
+  const uint32_t xrow = (uint32_t)d * 2u;
+  Stream<kAuxCached, kAuxStream, KRows, KRows> st;
+  st.init(dz + t0 * kRowsA, (uint32_t)(t1 - t0) * (uint32_t)(kRowsA * 2), (uint32_t)(kRowsA * 2), x + t0 * d + n0,
+          (uint32_t)((t1 - t0) * xrow - 2 * n0), xrow, (int)(s1 - s0), wave, lane, Slots{xs0, xs1, xs2, ws0, ws1});
+  st.prologue();
+  f32x16 acc[kMB][kNB];
+  st.run(acc, wave, lane);
+  float* const stage = reinterpret_cast<float*>(wave == 0 ? xs0 : wave == 1 ? xs1 : wave == 2 ? xs2 : ws0);
+  store_tile(acc, stage, part + (int64_t)z * kRowsA * d, d, 0, n0, kRowsA, d, wave, lane);
+}
+
+// out[i] = sum_{s < S} part[s * stride + i], in order s = 0, 1, ... (0 for S = 0); n4 float4s.
 __global__ __launch_bounds__(256) void reduce_partials_kernel(const float4* __restrict__ part, int S, int64_t stride4,
                                                               int64_t n4, float4* __restrict__ out) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
-    float4 a = part[i];
-    for (int s = 1; s < S; ++s) {
+    float4 a = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s = 0; s < S; ++s) {
       const float4 b = part[s * stride4 + i];
       a.x += b.x;
       a.y += b.y;
@@ -275,97 +404,66 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(const float4* __re
 }
 
 template <int K>
-hipError_t launch_grad_logits_k(const BackwardArgs& a, const BackwardPlan& p, hipStream_t s) {
-  const dim3 grid((unsigned)(p.T_pad / kRowsB));
-  const float zc2 = a.T > 0 ? 2.0f * a.zloss_coef / (float)a.T : 0.0f;
+hipError_t launch_grad_k(const BackwardArgs& a, const BackwardPlan& p, hipStream_t s) {
+  const dim3 grid((unsigned)((a.T + kRowsB - 1) / kRowsB));
+  const float zc2 = 2.0f * a.zloss_coef / (float)a.T;
+  uint16_t* const dz = a.dw != nullptr ? p.dz : nullptr;
   if (a.n_experts == kRowsA)
-    return launch(grad_logits_kernel<K, true>, grid, dim3(kThreads), 0, s, (const uint16_t*)a.x, (const uint16_t*)a.w,
-                  a.T, a.d, a.n_experts, a.normalize, a.idx, a.dgates, zc2, p.dzt, p.T_pad);
-  return launch(grad_logits_kernel<K, false>, grid, dim3(kThreads), 0, s, (const uint16_t*)a.x, (const uint16_t*)a.w,
-                a.T, a.d, a.n_experts, a.normalize, a.idx, a.dgates, zc2, p.dzt, p.T_pad);
-}
-
-hipError_t launch_transpose(const uint16_t* in, int64_t R, int64_t R_pad, int64_t C, int64_t ldi, uint16_t* out,
-                            int64_t ldo, hipStream_t s) {
-  return launch(transpose_bf16_kernel, dim3((unsigned)(R_pad / 64), (unsigned)(C / 64)), dim3(256), 0, s, in, R, C, ldi,
-                out, ldo);
+    return launch(grad_kernel<K, true>, grid, dim3(kThreads), 0, s, (const uint16_t*)a.x, (const uint16_t*)a.w, a.T,
+                  a.d, a.n_experts, a.normalize, a.idx, a.dgates, zc2, dz, a.dx);
+  return launch(grad_kernel<K, false>, grid, dim3(kThreads), 0, s, (const uint16_t*)a.x, (const uint16_t*)a.w, a.T,
+                a.d, a.n_experts, a.normalize, a.idx, a.dgates, zc2, dz, a.dx);
 }
 
 }  // namespace
 
 BackwardPlan backward_plan(int64_t T, int d, void* workspace) {
   BackwardPlan p{};
-  p.T_pad = (T + kRowsB - 1) / kRowsB * kRowsB;
-  if (p.T_pad == 0) p.T_pad = kRowsB;
-  // Token chunks of dW: 256 c tokens with c <= 8 the largest divisor of T_pad / 256, so the
-  // chunks tile the padded rows exactly (a chunk must never run into the next row).
-  const int64_t q = p.T_pad / kRowsB;
-  int64_t c = 8;
-  while (q % c != 0) --c;
-  p.k_chunk = kRowsB * c;
-  p.splits = (int)(q / c);
+  p.Q = (T + kBK - 1) / kBK;
+  p.n_col = (d + kRowsB - 1) / kRowsB;
+  // Token ranges of dW: enough for one workgroup per CU, each range's X rows under 2 GiB (the
+  // buffer descriptors' 32-bit range), never more ranges than 64-token stages.
+  int64_t S = kCtas / p.n_col > 1 ? kCtas / p.n_col : 1;
+  const int64_t need = (T * (int64_t)d + (int64_t(1) << 30) - 1) >> 30;
+  if (S < need) S = need;
+  if (S > p.Q) S = p.Q;
+  p.splits = (int)S;
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
-  size_t off = 0;
-  const size_t dzt_b = al((size_t)kRowsA * p.T_pad * 2), dz_b = dzt_b, wt_b = al((size_t)d * kRowsA * 2);
-  const size_t xt_b = al((size_t)d * p.T_pad * 2), part_b = al((size_t)p.splits * kRowsA * d * 4);
   unsigned char* base = static_cast<unsigned char*>(workspace);
-  p.dzt = reinterpret_cast<uint16_t*>(base + off);
-  off += dzt_b;
+  size_t off = 0;
   p.dz = reinterpret_cast<uint16_t*>(base + off);
-  off += dz_b;
-  p.wt = reinterpret_cast<uint16_t*>(base + off);
-  off += wt_b;
-  p.xt = reinterpret_cast<uint16_t*>(base + off);
-  off += xt_b;
+  off += al((size_t)T * kRowsA * 2);
   p.part = reinterpret_cast<float*>(base + off);
-  off += part_b;
-  p.bytes = off;
+  off += al((size_t)p.splits * kRowsA * d * 4);
+  p.bytes = off > 0 ? off : 256;
   return p;
 }
 
 hipError_t launch_router_backward(const BackwardArgs& a, const BackwardPlan& p, hipStream_t s) {
-  hipError_t err;
-  switch (a.k) {
-    case 1: err = launch_grad_logits_k<1>(a, p, s); break;
-    case 2: err = launch_grad_logits_k<2>(a, p, s); break;
-    case 3: err = launch_grad_logits_k<3>(a, p, s); break;
-    case 4: err = launch_grad_logits_k<4>(a, p, s); break;
-    case 5: err = launch_grad_logits_k<5>(a, p, s); break;
-    case 6: err = launch_grad_logits_k<6>(a, p, s); break;
-    case 7: err = launch_grad_logits_k<7>(a, p, s); break;
-    default: err = launch_grad_logits_k<8>(a, p, s); break;
-  }
-  if (err != hipSuccess) return err;
-  const int64_t d = a.d;
-  // dZ [T_pad][256] from dZ^T; W^T [d][256] (experts past n_experts zero); X^T [d][T_pad].
-  if ((err = launch_transpose(p.dzt, kRowsA, kRowsA, p.T_pad, p.T_pad, p.dz, kRowsA, s)) != hipSuccess) return err;
-  if ((err = launch_transpose((const uint16_t*)a.w, a.n_experts, kRowsA, d, d, p.wt, kRowsA, s)) != hipSuccess)
-    return err;
-  if (a.dw != nullptr &&
-      (err = launch_transpose((const uint16_t*)a.x, a.T, p.T_pad, d, d, p.xt, p.T_pad, s)) != hipSuccess)
-    return err;
-  if (a.dx != nullptr && a.T > 0) {
-    // dX [T][d] = dZ W: A = dZ rows (tokens), B = W^T rows (columns of d), K = 256 experts.
-    err = launch(gemm_nt_kernel, dim3((unsigned)(p.T_pad / kRowsA), (unsigned)((d + kRowsB - 1) / kRowsB), 1),
-                 dim3(kThreads), 0, s,
-                 (const uint16_t*)p.dz, p.T_pad, (const uint16_t*)p.wt, d, (int64_t)kRowsA, kRowsA / kBK, a.dx, a.T, d,
-                 d, (int64_t)0);
+  hipError_t err = hipSuccess;
+  if (a.T > 0) {
+    switch (a.k) {
+      case 1: err = launch_grad_k<1>(a, p, s); break;
+      case 2: err = launch_grad_k<2>(a, p, s); break;
+      case 3: err = launch_grad_k<3>(a, p, s); break;
+      case 4: err = launch_grad_k<4>(a, p, s); break;
+      case 5: err = launch_grad_k<5>(a, p, s); break;
+      case 6: err = launch_grad_k<6>(a, p, s); break;
+      case 7: err = launch_grad_k<7>(a, p, s); break;
+      default: err = launch_grad_k<8>(a, p, s); break;
+    }
     if (err != hipSuccess) return err;
   }
-  if (a.dw != nullptr) {
-    // dW [n_experts][d] = dZ^T X: A = dZ^T rows (experts), B = X^T rows (columns of d), K = tokens,
-    // split into chunks of k_chunk tokens; the partials are then summed in chunk order.
-    err = launch(gemm_nt_kernel, dim3(1, (unsigned)((d + kRowsB - 1) / kRowsB), (unsigned)p.splits), dim3(kThreads), 0,
-                 s,
-                 (const uint16_t*)p.dzt, (int64_t)kRowsA, (const uint16_t*)p.xt, d, p.T_pad, (int)(p.k_chunk / kBK),
-                 p.part, (int64_t)kRowsA, d, d, (int64_t)kRowsA * d);
+  if (a.dw == nullptr) return err;
+  if (a.T > 0) {
+    err = launch(dw_kernel, dim3((unsigned)(p.n_col * p.splits)), dim3(kThreads), 0, s, (const uint16_t*)p.dz,
+                 (const uint16_t*)a.x, a.T, a.d, p.Q, p.splits, p.n_col, p.part);
     if (err != hipSuccess) return err;
-    const int64_t n4 = (int64_t)a.n_experts * d / 4;
-    const int64_t blocks = (n4 + 255) / 256 < 2048 ? (n4 + 255) / 256 : 2048;
-    err = launch(reduce_partials_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const float4*)p.part, p.splits,
-                 (int64_t)kRowsA * d / 4, n4, (float4*)a.dw);
   }
-  return err;
+  const int64_t n4 = (int64_t)a.n_experts * a.d / 4;
+  const int64_t blocks = (n4 + 255) / 256 < 2048 ? (n4 + 255) / 256 : 2048;
+  return launch(reduce_partials_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const float4*)p.part,
+                a.T > 0 ? p.splits : 0, (int64_t)kRowsA * a.d / 4, n4, (float4*)a.dw);
 }
 
 }  // namespace elb

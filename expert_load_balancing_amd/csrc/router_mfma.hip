@@ -86,8 +86,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // ---- operand streams: start the DMA ring (A = weights, B = this tile's tokens) ----
   const uint32_t row_bytes = (uint32_t)d * 2u;
   Stream<kAuxCached, kAuxStream> st;
-  st.init(w, (uint32_t)n_experts * row_bytes, x + row0 * d, (uint32_t)rows * row_bytes, row_bytes, d / kBK, wave,
-          lane, Slots{xs0, xs1, xs2, ws0, ws1});
+  st.init(w, (uint32_t)n_experts * row_bytes, row_bytes, x + row0 * d, (uint32_t)rows * row_bytes, row_bytes,
+          d / kBK, wave, lane, Slots{xs0, xs1, xs2, ws0, ws1});
   st.prologue();
 
   // ---- shifted bias b' = b + (1 - min b) >= 1, so every selection key is a positive float ----

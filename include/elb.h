@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define ELB_VERSION 10300 /* major * 10000 + minor * 100 + patch */
+#define ELB_VERSION 10400 /* major * 10000 + minor * 100 + patch */
 
 typedef struct ihipStream_t* elb_stream_t; /* hipStream_t; NULL = default stream */
 

@@ -228,14 +228,16 @@ def test_route_step_zloss_needs_lse(lib):
 
 
 def test_backward_workspace_size(lib):
-    # dz^T + dz (256 x T_pad bf16 each), W^T (d x 256 bf16), X^T (d x T_pad bf16), dW partials
-    # (splits x 256 x d fp32), each rounded up to 256 bytes.  T_pad = 65536: 32 chunks of 2048.
-    T_pad, d = 65536, 3072
-    want = 2 * 256 * T_pad * 2 + d * 256 * 2 + d * T_pad * 2 + 32 * 256 * d * 4
-    assert lib.elb_backward_workspace_bytes(65536, 3072, 256) == want
-    # 2100 tokens -> T_pad 2304 = 9 tiles -> chunks of 3 tiles (768 tokens), 3 partials.
-    assert lib.elb_backward_workspace_bytes(2100, 192, 64) == 2 * 256 * 2304 * 2 + 192 * 256 * 2 + 192 * 2304 * 2 + \
-        3 * 256 * 192 * 4
+    # dZ token-major (T x 256 bf16), then the dW partials (splits x 256 x d fp32), each rounded
+    # up to 256 bytes.  splits = 256 // ceil(d / 256) token ranges (one workgroup per CU), at
+    # most ceil(T / 64).  d = 3072: 12 column tiles -> 21 ranges.
+    assert lib.elb_backward_workspace_bytes(65536, 3072, 256) == 65536 * 512 + 21 * 256 * 3072 * 4
+    # 2100 tokens, d = 192: 1 column tile -> 256 ranges wanted, 33 stages of 64 tokens -> 33.
+    assert lib.elb_backward_workspace_bytes(2100, 192, 64) == 2100 * 512 + 33 * 256 * 192 * 4
+    # 1 token: one range; the dZ row rounds up to 512 bytes.
+    assert lib.elb_backward_workspace_bytes(1, 64, 8) == 512 + 256 * 64 * 4
+    # No tokens: a minimal workspace (nothing of it is read).
+    assert lib.elb_backward_workspace_bytes(0, 64, 8) == 256
     assert lib.elb_backward_workspace_bytes(-1, 64, 8) == 0
     assert lib.elb_backward_workspace_bytes(100, 100, 8) == 0
     assert lib.elb_backward_workspace_bytes(100, 64, 300) == 0

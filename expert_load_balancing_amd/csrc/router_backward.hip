@@ -52,6 +52,7 @@ __device__ __forceinline__ float sigmoid_fast(float z) {
 }
 
 constexpr int kDxStores = 16;  // stores per wave per dX stage: 64 tokens x 64 columns fp32, 1 KiB each
+static_assert(kDma + 2 * kDxStores <= 63, "vmcnt budget fits the counter");
 constexpr int kDxAhead = 3;  // k-blocks of W fragments read ahead (4 reads each, <= 15 in flight)
 
 // One 256-token tile: dZ [t][256] (bf16, token-major; NULL: not stored) and dX [t][d] (fp32;
@@ -196,15 +197,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // slots are free and the vmcnt budgets below start from zero.
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0) & ~(15 << 8));
   bare_barrier();
-  // W slots xs0 / xs1: 256 expert rows x 64 columns (128 bytes), rows past n_experts read 0.
-  // Chunks of row r sit at chunk ^ (((r >> 1) & 1) << 2): a transposed read has each group of
-  // 32 lanes read 4 consecutive rows (two per 256-byte bank window) x 64 bytes, and the swizzle
-  // puts rows r and r + 2 in different halves of their window.  Store stage: xs2, 8 KiB a wave.
+  // W slots xs0, xs1, ws0 (a ring; stage j + 2 fills while stage j is read): 256 expert rows x
+  // 64 columns (128 bytes), rows past n_experts read 0.  Chunks of row r sit at
+  // chunk ^ (((r >> 1) & 1) << 2): a transposed read has each group of 32 lanes read 4
+  // consecutive rows (two per 256-byte bank window) x 64 bytes, and the swizzle puts rows r and
+  // r + 2 in different halves of their window.  Store stage: xs2, 8 KiB a wave.
   //
-  // Ordering.  The compiler makes a transposed LDS read wait for every LDS DMA issued before it
-  // (the read carries no alias information), so stage j + 1's DMAs go out only after stage j's
-  // last read: one slot is read while the other fills.  Stage j then needs only its own DMAs,
-  // behind which come the 16 stores of stage j - 1: vmcnt(16) leaves those stores in flight.
+  // vmcnt budget when stage j's DMAs must have landed: per stage a wave issues 8 DMAs (stage
+  // j + 2) and then kDxStores stores (stage j); behind stage j's DMAs come those of stage 1
+  // (j = 0), the DMAs of stage 2 and the stores of stage 0 (j = 1), or the stores of j - 2, the
+  // DMAs of j + 1 and the stores of j - 1 (j >= 2).  Stages 0 and 1 are peeled: one loop over
+  // three different waits would leave the compiler's own wait analysis with the weakest.
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, (uint32_t)n_experts * row_bytes);
   uint32_t vo[kDma];
 #pragma unroll
@@ -214,14 +217,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   }
   const uint32_t wave_off = (uint32_t)wave * (64 * kRowB);
   const int nst = d / kBK;
+  const __amdgpu_buffer_rsrc_t none = make_rsrc(w, 0u);
+  // Stage offsets are forced wave-uniform with readfirstlane: a vector offset would turn every
+  // DMA and store into a loop over distinct lane values.
   auto dma = [&](unsigned char* slot, int j) {
-    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)j * kRowB);  // scalar: see below
-#pragma unroll
-    for (int i = 0; i < kDma; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, ELB_AS3(slot + wave_off + i * 1024), 16, vo[i], (int)soff, 0,
-                                               kAuxCached);
+    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)j * kRowB);
+    dma_rows<kAuxCached>(wr, none, slot + wave_off, vo, soff, j < nst);
   };
   dma(xs0, 0);
+  dma(xs1, 1);
   // Stores go through a descriptor covering the tile's live rows: rows past T are dropped while
   // every store instruction still issues (the vmcnt budget counts them).  They are non-temporal:
   // with normal allocation the dX stream would push W out of L2, where every CU re-reads it.
@@ -239,7 +243,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const unsigned char* p = sl + kb * (16 * kRowB) + ro + (((uint32_t)cb << 6) ^ sw);
     return join_tr(ds_read_tr16(p), ds_read_tr16(p + 8 * kRowB));
   };
-  // Stage j: multiply the W columns in `cur`, start stage j + 1's DMAs into `nxt`, store.
+  // Stage j: start stage j + 2's DMAs into `nxt`, multiply the W columns in `cur`, store.
   auto stage = [&](int j, const unsigned char* cur, unsigned char* nxt) {
     f32x16 c[2][kNB];
 #pragma unroll
@@ -248,6 +252,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) c[cb][nb][r] = 0.0f;
+    dma(nxt, j + 2);
     // Fragments run kDxAhead k-blocks ahead of the MFMAs that use them: 4 MFMAs (128 cycles) per
     // k-block do not cover an LDS read's latency while four waves share the LDS.
     bf16x8 a[kDxAhead + 1][2];
@@ -279,8 +284,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       if (kb + kDxAhead < 16) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    if (j + 1 < nst) dma(nxt, j + 1);
     // Stores go out as whole 256-byte row segments, one 32-column half of the 64 x 64 fp32 tile
     // at a time through the wave's LDS stage: [64 tokens][8 chunks of 16 bytes], chunk ch of
     // token row t at ch ^ (t & 7).  Lane: token 32 nb + l32 of the wave; accumulator 4 g + r:
@@ -307,20 +310,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       }
     }
   };
-  // Stage 0 needs only its own DMAs; stage j >= 1 has the 16 stores of stage j - 1 behind them.
-  // (Offsets are forced wave-uniform with readfirstlane: a vector offset would turn every DMA and
-  // store into a loop over distinct lane values.)
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0) & ~(15 << 8));
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDma) & ~(15 << 8));
   bare_barrier();
-  stage(0, xs0, xs1);
-  for (int j = 1; j < nst; j += 2) {
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDxStores) & ~(15 << 8));
+  stage(0, xs0, ws0);
+  if (nst > 1) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDma + kDxStores) & ~(15 << 8));
     bare_barrier();
-    stage(j, xs1, xs0);
+    stage(1, xs1, xs0);
+  }
+  for (int j = 2; j < nst; j += 3) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDma + 2 * kDxStores) & ~(15 << 8));
+    bare_barrier();
+    stage(j, ws0, xs1);
     if (j + 1 >= nst) break;
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDxStores) & ~(15 << 8));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDma + 2 * kDxStores) & ~(15 << 8));
     bare_barrier();
-    stage(j + 1, xs0, xs1);
+    stage(j + 1, xs0, ws0);
+    if (j + 2 >= nst) break;
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDma + 2 * kDxStores) & ~(15 << 8));
+    bare_barrier();
+    stage(j + 2, xs1, xs0);
   }
   // The stores drain before the workgroup ends.
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0) & ~(15 << 8));

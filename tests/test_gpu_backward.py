@@ -50,7 +50,9 @@ def check(got, ref, bound, what):
     (513, 64, 16, 2, True, 1e-2),
     (1024, 512, 256, 8, True, 0.1),
     (1, 64, 8, 1, True, 0.0),
-    (2100, 192, 64, 4, False, 0.0),   # d not a multiple of 256, token chunks of 768
+    (2100, 192, 64, 4, False, 0.0),   # d not a multiple of 256: one column tile, 33 token ranges
+    (777, 320, 256, 4, True, 0.05),   # two column tiles, the second with 64 live columns
+    (4113, 1088, 128, 2, False, 0.0),  # 5 column tiles -> 51 token ranges of 1-2 stages
 ])
 def test_backward_matches_oracle(T, d, n_e, k, normalize, zc):
     log(f"backward T={T} d={d} N_r={n_e} K={k} normalize={normalize} zloss={zc}")

@@ -127,3 +127,36 @@ def test_backward_full_size_sampled():
     dz2 = oracle.logit_grads(oracle.router_logits(x[:T2], w), idx2, G2, normalize=True, zloss_coef=1e-2)
     x64 = oracle.widen(x[:T2])
     check(dw, dz2.T @ x64, (2.0 ** -8 + T2 * 2.0 ** -24) * (np.abs(dz2).T @ np.abs(x64)), "dw 16384 tokens")
+
+
+def test_backward_stress_size():
+    """The largest workload (T = 262144, d = 4096: 16 column tiles x 16 token ranges of 16384
+    tokens for dW), with the z-loss: dx on sampled tokens, dw against the oracle over the whole
+    batch, accumulated in 16384-token chunks (the chain rule is per token, dw a sum over them)."""
+    wl = datagen.WORKLOADS["stress"]
+    x, w, b = datagen.tokens(wl), datagen.router_weight(wl), datagen.initial_bias(wl)
+    log(f"backward stress T={wl.T} d={wl.d}")
+    zc = 1e-3
+    idx, G, dx, dw = run(x, w, b, wl.k, True, zc, seed=31)
+    w64 = oracle.widen(w)
+    rows = sample_rows(wl.T, 300, seed=5)
+    z = oracle.router_logits(x[rows], w)
+    dz = oracle.logit_grads(z, idx[rows], G[rows], normalize=True, zloss_coef=0.0)
+    zmax = z.max(axis=1, keepdims=True)
+    e = np.exp(z - zmax)
+    dz += zc * (2.0 / wl.T) * (zmax + np.log(e.sum(axis=1, keepdims=True))) * e / e.sum(axis=1, keepdims=True)
+    check(dx[rows], dz @ w64, (2.0 ** -8 + 256 * 2.0 ** -24) * (np.abs(dz) @ np.abs(w64)), "dx sampled")
+    ref = np.zeros((wl.n_experts, wl.d))
+    mag = np.zeros((wl.n_experts, wl.d))
+    C = 16384
+    for c0 in range(0, wl.T, C):
+        zc_ = oracle.router_logits(x[c0:c0 + C], w)
+        d_ = oracle.logit_grads(zc_, idx[c0:c0 + C], G[c0:c0 + C], normalize=True, zloss_coef=0.0)
+        zm = zc_.max(axis=1, keepdims=True)
+        ec = np.exp(zc_ - zm)
+        d_ += zc * (2.0 / wl.T) * (zm + np.log(ec.sum(axis=1, keepdims=True))) * ec / ec.sum(axis=1, keepdims=True)
+        xc = oracle.widen(x[c0:c0 + C])
+        ref += d_.T @ xc
+        mag += np.abs(d_).T @ np.abs(xc)
+    r = check(dw, ref, (2.0 ** -8 + wl.T * 2.0 ** -24) * mag, "dw whole batch")
+    log(f"  worst dw error / bound {r:.3f}")

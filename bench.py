@@ -108,7 +108,8 @@ def cpu_baseline(wl, x, w, b, m, min_seconds: float = 10.0, max_seconds: float =
             r = oracle.route(x, w, b, wl.k)
             n = oracle.expert_loads(r.idx, wl.n_experts)
             oracle.max_violation(n)
-            oracle.dispatch_permutation(r.idx, wl.n_experts)
+            if wl.dispatch:
+                oracle.dispatch_permutation(r.idx, wl.n_experts)
             oracle.balance_step(n, b, m, mode=wl.mode, lam=wl.lam, beta=wl.beta, kappa=wl.kappa, gamma=wl.gamma)
             reps += 1
             el = time.perf_counter() - t0
@@ -116,7 +117,7 @@ def cpu_baseline(wl, x, w, b, m, min_seconds: float = 10.0, max_seconds: float =
                 break
     return {"value": reps * wl.T / el, "unit": "routed tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"the full step of {wl.label} (route + loads + MaxVio"
-                      f" + dispatch + {wl.mode} update), {reps} repetition(s), "
+                      f"{' + dispatch' if wl.dispatch else ''} + {wl.mode} update), {reps} repetition(s), "
                       f"fp64 numpy, BLAS threads={cores}",
             "seconds": round(el, 2)}
 
@@ -150,7 +151,8 @@ def bench_next_rows(elb, wl, x, w, out, stream, reps: int = 20) -> dict:
     counts = torch.randint(0, 4 * T // n_e * 2, (L, n_e), dtype=torch.int32, device=x.device)
     bl, ml = torch.zeros((L, n_e), device=x.device), torch.zeros((L, n_e), device=x.device)
     res["update_60_layers_us"] = round(time_events(lambda: elb.smebu_update_layers(counts, bl, ml), reps, stream) * 1e3, 2)
-    inv = out.inv_perm.clone()
+    # The permutation of this batch (from the step, or from a dispatch call when the step has none).
+    inv = out.inv_perm.clone() if out.inv_perm is not None else elb.router_dispatch(out.topk_idx, n_e)[2]
     gates = out.gates.clone()
     xp = torch.empty((T * k, d), dtype=x.dtype, device=x.device)
     y = torch.empty((T, d), dtype=torch.float32, device=x.device)
@@ -229,8 +231,10 @@ def main() -> int:
     wd, bd, md = to_dev(w), to_dev(b0), to_dev(m0)
     T, d, n_e, k = wl.T, wl.d, wl.n_experts, wl.k
     # One library call per step (elb_route_step): router kernel, dispatch scan with the bias
-    # update beside it, scatter.  The loads accumulate into counts and the update clears them.
-    step = elb.RouterStep(wd, bd, md, k, T, mode=wl.mode, lam=wl.lam, beta=wl.beta, kappa=wl.kappa, gamma=wl.gamma)
+    # update beside it, scatter (workloads without dispatch: router kernel, then the update).
+    # The loads accumulate into counts and the update clears them.
+    step = elb.RouterStep(wd, bd, md, k, T, mode=wl.mode, lam=wl.lam, beta=wl.beta, kappa=wl.kappa, gamma=wl.gamma,
+                          dispatch=wl.dispatch)
     stream = torch.cuda.current_stream(dev)
 
     # Every `timing_every`-th timed step carries events around its router kernel (recorded by the
@@ -282,7 +286,7 @@ def main() -> int:
         "dtype": "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": wl.label, "T": T, "d": d, "n_experts": n_e, "k": k, "balance": wl.mode,
-                   "dispatch": True, "parallelism": "none (1 GPU)"},
+                   "dispatch": wl.dispatch, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else round(traffic),

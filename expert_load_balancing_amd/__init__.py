@@ -294,8 +294,8 @@ class StepOutputs(NamedTuple):
     topk_idx: torch.Tensor   # [T, k] int32
     gates: torch.Tensor      # [T, k] fp32
     counts: torch.Tensor     # [N_r] int32 (zero after a step that cleared them)
-    offsets: torch.Tensor    # [N_r + 1] int32
-    perm: torch.Tensor       # [T * k] int32
+    offsets: torch.Tensor | None  # [N_r + 1] int32 (None without dispatch)
+    perm: torch.Tensor | None     # [T * k] int32 (None without dispatch)
     inv_perm: torch.Tensor | None
     lse: torch.Tensor | None
     zloss: torch.Tensor | None
@@ -304,7 +304,8 @@ class StepOutputs(NamedTuple):
 
 
 class RouterStep:
-    """Route, dispatch and (optionally) update the expert bias in one library call (elb_route_step).
+    """Route, dispatch (optional) and update (optional) the expert bias in one library call
+    (elb_route_step).
 
     Holds the router weight w [N_r, d], the bias b [N_r] and momentum m [N_r] (updated in place
     when ``update``), and output buffers sized for up to ``max_tokens`` tokens, allocated once.
@@ -312,13 +313,14 @@ class RouterStep:
     current bias, then applies one bias update from this batch's loads and leaves the counts
     zeroed for the next call.  Without ``update`` the loads accumulate across calls (several
     micro-batches per optimizer step) until an update with ``clear_counts`` consumes them.
+    ``dispatch=False`` skips the counting-sort dispatch (offsets, perm, inv_perm are then None).
     """
 
     def __init__(self, w: torch.Tensor, bias: torch.Tensor, momentum: torch.Tensor | None, k: int, max_tokens: int,
                  *, update: bool = True, mode: str = "smebu", lam: float = 5e-4, beta: float = 0.5,
                  kappa: float = 2.0, gamma: float = 1e-3, clear_counts: bool = True, gates_raw: bool = False,
                  want_inv: bool = True, want_lse: bool = False, want_zloss: bool = False, want_delta: bool = False,
-                 want_maxvio: bool = True, force_generic: bool = False):
+                 want_maxvio: bool = True, force_generic: bool = False, dispatch: bool = True):
         _need(w, "w")
         dev = w.device
         if w.dtype not in _DTYPES:
@@ -337,23 +339,23 @@ class RouterStep:
         self.topk_idx = torch.empty((T, k), dtype=i32, device=dev)
         self.gates = torch.empty((T, k), dtype=f32, device=dev)
         self.counts = torch.zeros(n_e, dtype=i32, device=dev)
-        self.offsets = torch.empty(n_e + 1, dtype=i32, device=dev)
-        self.perm = torch.empty(T * k, dtype=i32, device=dev)
-        self.inv_perm = torch.empty(T * k, dtype=i32, device=dev) if want_inv else None
+        self.offsets = torch.empty(n_e + 1, dtype=i32, device=dev) if dispatch else None
+        self.perm = torch.empty(T * k, dtype=i32, device=dev) if dispatch else None
+        self.inv_perm = torch.empty(T * k, dtype=i32, device=dev) if (dispatch and want_inv) else None
         self.lse = torch.empty(T, dtype=f32, device=dev) if (want_lse or want_zloss) else None
         self.zloss = torch.empty(1, dtype=f32, device=dev) if want_zloss else None
         self.delta_b = torch.empty(n_e, dtype=f32, device=dev) if (update and want_delta) else None
         self.maxvio = torch.empty(2, dtype=f32, device=dev) if (update and want_maxvio) else None
-        ws_bytes = dispatch_workspace_bytes(T, k, n_e)
-        self.workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        ws_bytes = dispatch_workspace_bytes(T, k, n_e) if dispatch else 0
+        self.workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev) if dispatch else None
         flags = ELB_ACCUMULATE_COUNTS | (ELB_GATES_RAW if gates_raw else 0) | (ELB_FORCE_GENERIC if force_generic else 0)
         a = StepArgs()
         a.dtype, a.d, a.w, a.bias = _DTYPES[w.dtype], d, w.data_ptr(), bias.data_ptr()
         a.n_experts, a.k, a.flags = n_e, k, flags
         a.topk_idx, a.gates, a.counts = self.topk_idx.data_ptr(), self.gates.data_ptr(), self.counts.data_ptr()
         a.logits, a.lse, a.zloss = None, _ptr(self.lse).value, _ptr(self.zloss).value
-        a.workspace, a.workspace_bytes = self.workspace.data_ptr(), self.workspace.numel()
-        a.offsets, a.perm, a.inv_perm = self.offsets.data_ptr(), self.perm.data_ptr(), _ptr(self.inv_perm).value
+        a.workspace, a.workspace_bytes = _ptr(self.workspace).value, 0 if self.workspace is None else self.workspace.numel()
+        a.offsets, a.perm, a.inv_perm = _ptr(self.offsets).value, _ptr(self.perm).value, _ptr(self.inv_perm).value
         a.update = 1 if update else 0
         a.params = BalanceParams(MODES[mode], lam, beta, kappa, gamma, ELB_CLEAR_COUNTS if clear_counts else 0)
         a.momentum, a.delta_b, a.maxvio = _ptr(momentum).value, _ptr(self.delta_b).value, _ptr(self.maxvio).value
@@ -382,6 +384,7 @@ class RouterStep:
         a.x, a.T = x.data_ptr(), T
         check("elb_route_step", lib().elb_route_step(ctypes.byref(a), _stream(self.device)))
         k = self.k
-        return StepOutputs(self.topk_idx[:T], self.gates[:T], self.counts, self.offsets, self.perm[:T * k],
+        return StepOutputs(self.topk_idx[:T], self.gates[:T], self.counts, self.offsets,
+                           None if self.perm is None else self.perm[:T * k],
                            None if self.inv_perm is None else self.inv_perm[:T * k],
                            None if self.lse is None else self.lse[:T], self.zloss, self.delta_b, self.maxvio)

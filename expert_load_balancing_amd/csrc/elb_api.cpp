@@ -114,9 +114,13 @@ elb_status elb_route_step(const elb_step_args* args, elb_stream_t stream) {
   elb_status st = check_forward(a.x, a.dtype, a.T, a.d, a.w, a.bias, a.n_experts, a.k, a.flags, a.topk_idx, a.gates,
                                 a.counts, a.logits, a.lse);
   if (st != ELB_OK) return st;
-  st = check_dispatch(a.topk_idx, a.T, a.k, a.n_experts, a.workspace, a.workspace_bytes, a.offsets, a.perm,
-                      a.inv_perm);
-  if (st != ELB_OK) return st;
+  // No dispatch outputs at all: route (and update) only.
+  const bool dispatch = a.offsets != nullptr || a.perm != nullptr || a.inv_perm != nullptr;
+  if (dispatch) {
+    st = check_dispatch(a.topk_idx, a.T, a.k, a.n_experts, a.workspace, a.workspace_bytes, a.offsets, a.perm,
+                        a.inv_perm);
+    if (st != ELB_OK) return st;
+  }
   if (a.update != 0) {
     st = check_update(a.counts, a.n_experts, a.params, a.bias, a.momentum, a.delta_b, a.maxvio);
     if (st != ELB_OK) return st;
@@ -134,7 +138,8 @@ elb_status elb_route_step(const elb_step_args* args, elb_stream_t stream) {
                      a.k,     a.flags,    a.topk_idx, a.gates, a.counts, a.logits, a.lse,
                      static_cast<int32_t*>(a.workspace), g.stride};
   const bool mfma = !(a.flags & ELB_FORCE_GENERIC) && elb::router_mfma_applies(ra);
-  if (!mfma) ra.tile_loads = nullptr;
+  const bool loads_ready = dispatch && mfma && elb::router_mfma_full_tile(a.T);  // the router fills the table
+  if (!loads_ready) ra.tile_loads = nullptr;
   if (a.timing != nullptr && hipEventRecord(static_cast<hipEvent_t>(a.timing[0]), s) != hipSuccess)
     return ELB_ERR_LAUNCH;
   if (a.T > 0) {
@@ -146,7 +151,8 @@ elb_status elb_route_step(const elb_step_args* args, elb_stream_t stream) {
   if (a.zloss != nullptr && elb::launch_zloss(a.lse, a.T, a.zloss, s) != hipSuccess) return ELB_ERR_LAUNCH;
   const elb::BalanceArgs upd =
       balance_args(a.counts, a.n_experts, a.params, a.bias, a.momentum, a.delta_b, a.maxvio);
-  return from_hip(elb::launch_dispatch(a.topk_idx, a.T, a.k, a.n_experts, a.workspace, mfma,
+  if (!dispatch) return a.update != 0 ? from_hip(elb::launch_balance(upd, s)) : ELB_OK;
+  return from_hip(elb::launch_dispatch(a.topk_idx, a.T, a.k, a.n_experts, a.workspace, loads_ready,
                                        a.update != 0 ? &upd : nullptr, a.offsets, a.perm, a.inv_perm, s));
 }
 

@@ -7,8 +7,9 @@
 // and B = a tile of tokens, both rows contiguous in k (the logits, transposed: Z^T = W X^T);
 // the router backward's dW = dZ^T X contracts over tokens with both operands k-major.
 //
-// Work decomposition: 4 waves, one per SIMD; wave w owns B rows 64 w .. 64 w + 63 against all
-// 256 A rows, i.e. 8 x 2 accumulators of 32 x 32 (256 AGPRs).  A 32 x 32 MFMA output puts one
+// Work decomposition: 4 waves, one per SIMD; wave w owns B rows 32 NB w .. + 32 NB - 1 against
+// all 256 A rows, i.e. 8 x NB accumulators of 32 x 32 (NB = 2: a 256 x 256 tile in 256 AGPRs;
+// NB = 1: a 256 x 128 tile, for batches too small to give every CU a 256-row B tile).  A 32 x 32 MFMA output puts one
 // B row per lane column: lane l holds column l % 32 of its block, and accumulator r holds A row
 // 8 (r / 4) + 4 (l / 32) + (r % 4).
 //
@@ -57,10 +58,7 @@ static_assert((kNX + kNW) * kSlot <= 160 * 1024, "LDS");
 constexpr int kDma = kSlot / (kWaves * 1024);  // DMA instructions per wave per slot (1 KiB each)
 
 static_assert(kNX == kPX + 1 && kNW == kPW + 1 && kUnroll % kNX == 0 && kUnroll % kNW == 0, "ring shape");
-static_assert(kPX >= kPW, "the vmcnt budget below assumes the B stream runs further ahead");
-// VMEM instructions a wave issues after the DMAs of stage j's A rows, when it must have stage j:
-// the B DMAs of the same iteration, then (kPW - 1) full iterations.
-constexpr int kVmBudget = kDma + 2 * kDma * (kPW - 1);
+static_assert(kPX >= kPW, "the vmcnt budget of Stream assumes the B stream runs further ahead");
 
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 constexpr int kWaitLgkm0 = 63 & 15 | (3 << 14) | (7 << 4);  // lgkmcnt(0) only
@@ -91,13 +89,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // instead put a VALU write to one shared register before every DMA, which stalls behind the
 // previous DMA's operand read whenever the vector memory queue is full, and with it every
 // MFMA queued behind.)
-template <int AUX>
+template <int AUX, int N>
 __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, __amdgpu_buffer_rsrc_t none,
-                                         unsigned char* wave_base, const uint32_t (&vo)[kDma], uint32_t soff,
+                                         unsigned char* wave_base, const uint32_t* vo, uint32_t soff,
                                          bool real) {
   const __amdgpu_buffer_rsrc_t use = real ? r : none;
 #pragma unroll
-  for (int i = 0; i < kDma; ++i)
+  for (int i = 0; i < N; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(use, ELB_AS3(wave_base + i * 1024), 16, vo[i], (int)soff, 0, AUX);
 }
 
@@ -121,11 +119,12 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 // one 16-byte read per lane: row l % 32, k 8 (l / 32) .. + 7.
 struct RowsK {
   static constexpr int kReads = 1;  // LDS reads per fragment
-  // DMA: instruction i of wave `wave` fills rows 64 wave + 8 i + lane / 8; lane position
-  // p = lane & 7 in the row receives the global chunk stored there, swz(row, p) (the swizzle is
-  // its own inverse).  One stage advances 128 bytes along every row.
-  __device__ static __forceinline__ uint32_t dma_off(int wave, int lane, int i, uint32_t row_bytes) {
-    const int r = wave * 64 + 8 * i + (lane >> 3);
+  // DMA: a wave fills `rows_wave` consecutive rows; its instruction i fills rows
+  // rows_wave * wave + 8 i + lane / 8; lane position p = lane & 7 in the row receives the global
+  // chunk stored there, swz(row, p) (the swizzle is its own inverse).  One stage advances 128
+  // bytes along every row.
+  __device__ static __forceinline__ uint32_t dma_off(int wave, int lane, int i, uint32_t row_bytes, int rows_wave) {
+    const int r = wave * rows_wave + 8 * i + (lane >> 3);
     return (uint32_t)r * row_bytes + (uint32_t)(swz(r, lane & 7) << 4);
   }
   __device__ static __forceinline__ uint32_t stage_bytes(uint32_t) { return kRowB; }
@@ -181,7 +180,7 @@ struct KRows {
   static constexpr int kReads = 2;
   // DMA: instruction i of wave `wave` fills k rows 16 wave + 2 i + lane / 32, lane position
   // p = lane & 31 receiving global chunk p ^ ((r & 3) << 2).  One stage advances 64 k rows.
-  __device__ static __forceinline__ uint32_t dma_off(int wave, int lane, int i, uint32_t row_bytes) {
+  __device__ static __forceinline__ uint32_t dma_off(int wave, int lane, int i, uint32_t row_bytes, int) {
     const int r = wave * 16 + 2 * i + (lane >> 5);
     return (uint32_t)r * row_bytes + (uint32_t)(((lane & 31) ^ ((r & 3) << 2)) << 4);
   }
@@ -203,13 +202,20 @@ struct KRows {
 };
 
 // The streaming product.  AUX_A / AUX_B: cache policies of the two streams; LA / LB: their
-// layouts.  A's rows are `a_row_bytes` apart, B's `b_row_bytes`; `nkb` stages of kBK elements
-// are contracted (nkb >= 1).
-template <int AUX_A, int AUX_B, class LA = RowsK, class LB = RowsK>
+// layouts; NB: 32-row blocks of B per wave.  A's rows are `a_row_bytes` apart, B's
+// `b_row_bytes`; `nkb` stages of kBK elements are contracted (nkb >= 1).
+template <int AUX_A, int AUX_B, class LA = RowsK, class LB = RowsK, int NB = kNB>
 struct Stream {
+  static_assert(NB == kNB || (NB == 1 && LB::kReads == 1), "a 128-row B tile is laid out rows-contiguous-in-k");
+  // DMA instructions per wave per stage (1 KiB each): A's 256 rows, B's 128 NB rows, over 4 waves.
+  static constexpr int kDmaA = kDma;
+  static constexpr int kDmaB = kDma * NB / kNB;
+  // VMEM instructions a wave issues after the DMAs of stage j's A rows, when it must have stage
+  // j: the B DMAs of the same iteration, then (kPW - 1) full iterations.
+  static constexpr int kBudget = kDmaB + (kDmaA + kDmaB) * (kPW - 1);
   __amdgpu_buffer_rsrc_t ar, br, none;
-  uint32_t voa[kDma], vob[kDma];
-  uint32_t wave_off, a_stage, b_stage;
+  uint32_t voa[kDmaA], vob[kDmaB];
+  uint32_t wave_off_a, wave_off_b, a_stage, b_stage;
   int nkb;
   Slots sl;
 
@@ -223,11 +229,11 @@ struct Stream {
     nkb = n_stages;
     sl = slots;
 #pragma unroll
-    for (int i = 0; i < kDma; ++i) {
-      voa[i] = LA::dma_off(wave, lane, i, a_row_bytes);
-      vob[i] = LB::dma_off(wave, lane, i, b_row_bytes);
-    }
-    wave_off = (uint32_t)wave * (64 * kRowB);  // 8 KiB: 64 rows x 128 B or 16 rows x 512 B
+    for (int i = 0; i < kDmaA; ++i) voa[i] = LA::dma_off(wave, lane, i, a_row_bytes, 64);
+#pragma unroll
+    for (int i = 0; i < kDmaB; ++i) vob[i] = LB::dma_off(wave, lane, i, b_row_bytes, 32 * NB);
+    wave_off_a = (uint32_t)wave * (kDmaA * 1024);  // A: 64 rows x 128 B or 16 rows x 512 B
+    wave_off_b = (uint32_t)wave * (kDmaB * 1024);
     a_stage = LA::stage_bytes(a_row_bytes);
     b_stage = LB::stage_bytes(b_row_bytes);
   }
@@ -238,16 +244,16 @@ struct Stream {
 #pragma unroll
     for (int vi = -kPX; vi < 0; ++vi) {
       if (vi + kPW >= 0)
-        dma_rows<AUX_A>(ar, none, sl.w((vi + kPW) % kNW) + wave_off, voa, (uint32_t)(vi + kPW) * a_stage,
+        dma_rows<AUX_A, kDmaA>(ar, none, sl.w((vi + kPW) % kNW) + wave_off_a, voa, (uint32_t)(vi + kPW) * a_stage,
                         vi + kPW < nkb);
-      dma_rows<AUX_B>(br, none, sl.x((vi + kPX) % kNX) + wave_off, vob, (uint32_t)(vi + kPX) * b_stage,
+      dma_rows<AUX_B, kDmaB>(br, none, sl.x((vi + kPX) % kNX) + wave_off_b, vob, (uint32_t)(vi + kPX) * b_stage,
                       vi + kPX < nkb);
     }
   }
 
   // acc <- the product over all nkb stages (after prologue()).  On return every DMA has landed
   // and every wave is past its last operand read (the slots may be reused).
-  __device__ __forceinline__ void run(f32x16 (&acc)[kMB][kNB], int wave, int lane) {
+  __device__ __forceinline__ void run(f32x16 (&acc)[kMB][NB], int wave, int lane) {
     typename LA::Lane la;
     typename LB::Lane lb;
     la.init(lane);
@@ -256,7 +262,7 @@ struct Stream {
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < kNB; ++nb)
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
 
@@ -270,25 +276,25 @@ struct Stream {
         if (j >= nkb) break;
         // Own DMAs of stage j are done; after the barrier everyone's are, and every wave has
         // finished reading stage j - 1, whose slots the DMAs below overwrite.
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kVmBudget) & ~(15 << 8));  // and lgkmcnt(0)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kBudget) & ~(15 << 8));  // and lgkmcnt(0)
         bare_barrier();
         // A DMAs at the head of the stage (they must precede this stage's B DMAs for the vmcnt
         // budget); the B DMAs are spread over the MFMA stream below, so that a DMA waiting for
         // room in the vector memory pipeline only delays MFMAs already queued.
-        dma_rows<AUX_A>(ar, none, sl.w((u + kPW) % kNW) + wave_off, voa, (uint32_t)(j + kPW) * a_stage,
+        dma_rows<AUX_A, kDmaA>(ar, none, sl.w((u + kPW) % kNW) + wave_off_a, voa, (uint32_t)(j + kPW) * a_stage,
                         j + kPW < nkb);
         __builtin_amdgcn_sched_barrier(0);
-        dma_rows<AUX_B>(br, none, sl.x((u + kPX) % kNX) + wave_off, vob, (uint32_t)(j + kPX) * b_stage,
+        dma_rows<AUX_B, kDmaB>(br, none, sl.x((u + kPX) % kNX) + wave_off_b, vob, (uint32_t)(j + kPX) * b_stage,
                         j + kPX < nkb);
         const unsigned char* ws = sl.w(u % kNW);
         const unsigned char* xs = sl.x(u % kNX);
         // Operand fragments are double-buffered: the LDS reads of k-step s + 1 go out before
         // the 16 MFMAs of k-step s, so their latency hides behind 512 MFMA cycles (one wave per
         // SIMD has no other wave to hide it).
-        bf16x8 a[2][kMB], b[2][kNB];
+        bf16x8 a[2][kMB], b[2][NB];
         auto fetch = [&](int buf, int s) {
 #pragma unroll
-          for (int nb = 0; nb < kNB; ++nb) b[buf][nb] = lb.frag(xs, wave * kNB + nb, s);
+          for (int nb = 0; nb < NB; ++nb) b[buf][nb] = lb.frag(xs, wave * NB + nb, s);
 #pragma unroll
           for (int mb = 0; mb < kMB; ++mb) a[buf][mb] = la.frag(ws, mb, s);
         };
@@ -300,15 +306,15 @@ struct Stream {
 #pragma unroll
           for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < kNB; ++nb)
+            for (int nb = 0; nb < NB; ++nb)
               acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][mb], b[s & 1][nb], acc[mb][nb], 0, 0, 0);
         }
         // Issue order for the scheduler: reads of steps 0 and 1; then per step its MFMAs with
         // kDma / kKSteps B DMAs slotted between them, and the reads of step s + 2.
-        static_assert(kDma % kKSteps == 0 && (kMB * kNB) % (kDma / kKSteps) == 0, "DMA interleave");
-        constexpr int kDmaPerStep = kDma / kKSteps;
-        constexpr int kMfmaPerDma = kMB * kNB / kDmaPerStep;
-        constexpr int kReadsStep = kMB * LA::kReads + kNB * LB::kReads;
+        static_assert(kDmaB % kKSteps == 0 && (kMB * NB) % (kDmaB / kKSteps) == 0, "DMA interleave");
+        constexpr int kDmaPerStep = kDmaB / kKSteps;
+        constexpr int kMfmaPerDma = kMB * NB / kDmaPerStep;
+        constexpr int kReadsStep = kMB * LA::kReads + NB * LB::kReads;
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * kReadsStep, 0);  // DS reads, steps 0 and 1
 #pragma unroll
         for (int s = 0; s < kKSteps; ++s) {

@@ -222,7 +222,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // DMA and store into a loop over distinct lane values.
   auto dma = [&](unsigned char* slot, int j) {
     const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)j * kRowB);
-    dma_rows<kAuxCached>(wr, none, slot + wave_off, vo, soff, j < nst);
+    dma_rows<kAuxCached, kDma>(wr, none, slot + wave_off, vo, soff, j < nst);
   };
   dma(xs0, 0);
   dma(xs1, 1);

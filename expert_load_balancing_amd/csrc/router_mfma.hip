@@ -13,7 +13,8 @@
 // Work decomposition
 //   One workgroup (4 waves, one per SIMD) owns a tile of 256 tokens x all 256 experts and
 //   keeps the 256x256 fp32 logit tile in registers (each wave: 256 experts x 64 tokens = 16
-//   accumulators of 32x32).  The contraction is written transposed, Z^T = W . X^T, so that the
+//   accumulators of 32x32).  Batches of at most 128 x 256 tokens (one 256-token tile per CU
+//   would leave CUs idle) take 128-token tiles instead: each wave 256 experts x 32 tokens.  The contraction is written transposed, Z^T = W . X^T, so that the
 //   32x32 MFMA output puts one token per lane column: a lane ends up holding 128 of the 256
 //   logits of each of its tokens, and the other 128 sit in lane ^ 32.  Top-K therefore needs
 //   no LDS round trip: a register-local selection over 128 values, then one cross-lane merge.
@@ -43,8 +44,8 @@ namespace {
 using namespace tile;  // the streaming product and its constants
 
 constexpr int kExp = kRowsA;              // experts per tile (padded)
-constexpr int kTokWave = kRowsWave;       // tokens per wave
-constexpr int kTile = kRowsB;             // tokens per workgroup
+constexpr int kTile = kRowsB;             // tokens per workgroup of the full tile (NB = 2)
+constexpr int kCus = 256;                 // compute units of the MI355X
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Sorted (descending) top-K insertion: the new j-th largest is med3(old (j-1)-th, old j-th, x).
@@ -59,7 +60,8 @@ __device__ __forceinline__ float sigmoid_fast(float z) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
 }
 
-template <int K, bool FULL, bool EXTRA>
+// NB: 32-token blocks per wave (tile of 128 NB tokens).
+template <int K, bool FULL, bool EXTRA, int NB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void router_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const float* __restrict__ bias, int64_t T, int d,
     int n_experts, int normalize, int32_t* __restrict__ idx_out, float* __restrict__ gates_out,
@@ -74,8 +76,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps LDS bases in SGPRs
   const int h = lane >> 5;
   const int l32 = lane & 31;
-  const int64_t row0 = (int64_t)blockIdx.x * kTile;
-  const int rows = (int)(T - row0 < kTile ? T - row0 : kTile);
+  constexpr int kTok = 4 * 32 * NB;  // tokens per workgroup
+  constexpr int kTokWave = 32 * NB;
+  const int64_t row0 = (int64_t)blockIdx.x * kTok;
+  const int rows = (int)(T - row0 < kTok ? T - row0 : kTok);
 
   // Bias loads go first: a load issued behind the DMA prologue would have to wait for it.
   // Each wave reads all of b (4 values per lane) to form min b without any LDS.
@@ -85,7 +89,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
   // ---- operand streams: start the DMA ring (A = weights, B = this tile's tokens) ----
   const uint32_t row_bytes = (uint32_t)d * 2u;
-  Stream<kAuxCached, kAuxStream> st;
+  Stream<kAuxCached, kAuxStream, RowsK, RowsK, NB> st;
   st.init(w, (uint32_t)n_experts * row_bytes, row_bytes, x + row0 * d, (uint32_t)rows * row_bytes, row_bytes,
           d / kBK, wave, lane, Slots{xs0, xs1, xs2, ws0, ws1});
   st.prologue();
@@ -97,7 +101,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const float shift = 1.0f - mn;  // identical in every wave: min is exact
   const float bv = tid < n_experts ? bias[tid] : 0.0f;
 
-  f32x16 acc[kMB][kNB];
+  f32x16 acc[kMB][NB];
   st.run(acc, wave, lane);
 
   // ---- epilogue ----
@@ -113,7 +117,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // Output layout of a 32x32 MFMA block (rows = experts, columns = tokens): lane column l32 is
   // the token; accumulator r holds expert row 8 (r / 4) + 4 h + (r % 4).
 #pragma unroll
-  for (int nb = 0; nb < kNB; ++nb) {
+  for (int nb = 0; nb < NB; ++nb) {
     const int64_t t = row0 + wave * kTokWave + nb * 32 + l32;
     float top[K];
 #pragma unroll
@@ -225,22 +229,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   if (tid < n_experts) {
     const int n = hist[tid];
     if (n != 0) atomicAdd(&counts[tid], n);
-    // This tile's loads for the dispatch scan (the workgroup is the dispatch tile).
-    if (tile_loads != nullptr) tile_loads[(int64_t)tid * loads_stride + blockIdx.x] = n;
+    // This tile's loads for the dispatch scan (the full tile is the dispatch tile; the launcher
+    // passes no table with the half tile).
+    if (NB == kNB && tile_loads != nullptr) tile_loads[(int64_t)tid * loads_stride + blockIdx.x] = n;
   }
+}
+
+template <int K, bool FULL, int NB>
+hipError_t launch_kfn(const RouterArgs& a, hipStream_t stream) {
+  const int normalize = (a.flags & ELB_GATES_RAW) ? 0 : 1;
+  constexpr int kTok = 4 * 32 * NB;
+  const dim3 grid((unsigned)((a.T + kTok - 1) / kTok));
+  int32_t* const loads = NB == kNB ? a.tile_loads : nullptr;
+  if (a.logits != nullptr || a.lse != nullptr)
+    return launch(router_mfma_kernel<K, FULL, true, NB>, grid, dim3(kThreads), 0, stream, (const uint16_t*)a.x,
+                  (const uint16_t*)a.w, a.bias, a.T, a.d, a.n_experts, normalize, a.idx, a.gates, a.counts,
+                  a.logits, a.lse, loads, a.loads_stride);
+  return launch(router_mfma_kernel<K, FULL, false, NB>, grid, dim3(kThreads), 0, stream, (const uint16_t*)a.x,
+                (const uint16_t*)a.w, a.bias, a.T, a.d, a.n_experts, normalize, a.idx, a.gates, a.counts,
+                a.logits, a.lse, loads, a.loads_stride);
 }
 
 template <int K, bool FULL>
 hipError_t launch_kf(const RouterArgs& a, hipStream_t stream) {
-  const int normalize = (a.flags & ELB_GATES_RAW) ? 0 : 1;
-  const dim3 grid((unsigned)((a.T + kTile - 1) / kTile));
-  if (a.logits != nullptr || a.lse != nullptr)
-    return launch(router_mfma_kernel<K, FULL, true>, grid, dim3(kThreads), 0, stream, (const uint16_t*)a.x,
-                  (const uint16_t*)a.w, a.bias, a.T, a.d, a.n_experts, normalize, a.idx, a.gates, a.counts,
-                  a.logits, a.lse, a.tile_loads, a.loads_stride);
-  return launch(router_mfma_kernel<K, FULL, false>, grid, dim3(kThreads), 0, stream, (const uint16_t*)a.x,
-                (const uint16_t*)a.w, a.bias, a.T, a.d, a.n_experts, normalize, a.idx, a.gates, a.counts,
-                a.logits, a.lse, a.tile_loads, a.loads_stride);
+  return router_mfma_full_tile(a.T) ? launch_kfn<K, FULL, kNB>(a, stream) : launch_kfn<K, FULL, 1>(a, stream);
 }
 
 template <int K>
@@ -250,7 +262,9 @@ hipError_t launch_k(const RouterArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-static_assert(kTile == kDispatchTile, "the router tile must be the dispatch tile");
+static_assert(kTile == kDispatchTile, "the router's full tile must be the dispatch tile");
+
+bool router_mfma_full_tile(int64_t T) { return T > (int64_t)(kTile / 2) * kCus; }
 
 bool router_mfma_applies(const RouterArgs& a) {
   return a.dtype == ELB_BF16 && a.d % kBK == 0 && a.n_experts <= kExp && a.k >= 1 && a.k <= 8 &&

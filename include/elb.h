@@ -161,6 +161,10 @@ elb_status elb_smebu_update(int32_t* counts, int32_t n_experts, elb_balance_para
  * `bias` only after the router kernel has read it, so the next step routes with the new bias.
  * A training loop with one batch per optimizer step sets ELB_ACCUMULATE_COUNTS and
  * ELB_CLEAR_COUNTS and never resets `counts` itself (they must start at zero).
+ * offsets, perm and inv_perm all NULL: no dispatch (workspace is then not used); the update,
+ * if any, runs as its own launch after the router kernel.
+ * The MFMA router takes 128-token tiles for batches of at most 128 x 256 tokens (so that every
+ * compute unit gets a tile); the dispatch then counts the loads itself.
  * timing: NULL, or two hipEvent_t recorded on `stream` right before and right after the
  * router kernel (a measuring aid; both must be valid events).
  */

@@ -140,6 +140,10 @@ def step_args(**kw):
     # update checks, only when the update is asked for
     (dict(p_mode=7), UNSUPPORTED), (dict(p_flags=4), UNSUPPORTED), (dict(momentum=None), NULL),
     (dict(momentum=None, p_mode=1, p_flags=0, update=1, bias=FAKE + 1), ALIGN),
+    # no dispatch (offsets, perm, inv_perm all NULL): the forward and update checks still apply
+    (dict(offsets=None, perm=None, workspace=None, k=9), SHAPE),
+    (dict(offsets=None, perm=None, workspace=None, momentum=None), NULL),
+    (dict(offsets=None, perm=None, workspace=None, x=FAKE + 8), ALIGN),
 ])
 def test_route_step_rejects(lib, kw, want):
     assert lib.elb_route_step(ctypes.byref(step_args(**kw)), None) == want

@@ -136,3 +136,24 @@ def test_step_timing_events():
     step.set_timing(None)
     step(xd)
     torch.cuda.synchronize()
+
+
+def test_route_step_without_dispatch_matches():
+    """offsets, perm and inv_perm all NULL: the step routes and updates exactly as with the
+    dispatch (same idx, gates, counts, bias, momentum), and produces no permutation."""
+    for T in (5000, 40000):  # a 128-token tile batch and a 256-token tile batch
+        wl = datagen.WORKLOADS["large"].replace(T=T, d=512, seed=T, n_clusters=8)
+        x, w, b = datagen.tokens(wl), datagen.router_weight(wl), datagen.initial_bias(wl)
+        res = []
+        for dispatch in (True, False):
+            bd, md = to_dev(b), torch.zeros(wl.n_experts, device="cuda")
+            step = elb.RouterStep(to_dev(w), bd, md, wl.k, T, dispatch=dispatch, want_delta=True)
+            out = step(to_dev(x))
+            torch.cuda.synchronize()
+            res.append((out.topk_idx.cpu().numpy(), out.gates.cpu().numpy(), out.delta_b.cpu().numpy(),
+                        bd.cpu().numpy(), md.cpu().numpy(), out.maxvio.cpu().numpy()))
+            if not dispatch:
+                assert out.offsets is None and out.perm is None and out.inv_perm is None
+        for a, c in zip(res[0], res[1]):
+            assert np.array_equal(a, c)
+        log(f"T={T}: identical with and without dispatch")

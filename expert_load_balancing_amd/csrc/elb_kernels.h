@@ -43,7 +43,7 @@ struct BalanceArgs {
   float* maxvio;
 };
 
-// Launch `kernel` and return the runtime's verdict instead of dropping it.
+// Launch `kernel` and return the runtime's launch status instead of dropping it.
 template <typename... KArgs, typename... Args>
 hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem, hipStream_t stream,
                   Args&&... args) {

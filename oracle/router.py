@@ -16,7 +16,7 @@ Definitions followed
   * gates: from s_{i,t} only, never from b ("SMEBU Load Balancing", "How it works";
     Technical Report section 2.3 "normalized scores").
 
-Readings where the pages leave a step open (each also listed in the design doc):
+Readings where the pages leave a step open:
   * the hotdry blog places the bias before the sigmoid; the study note and the report
     summary place it on the score used by Top-K.  We add it after the sigmoid;
   * "normalized scores": by default gates are the selected scores divided by their sum

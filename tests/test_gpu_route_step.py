@@ -157,3 +157,19 @@ def test_route_step_without_dispatch_matches():
         for a, c in zip(res[0], res[1]):
             assert np.array_equal(a, c)
         log(f"T={T}: identical with and without dispatch")
+
+
+@pytest.mark.parametrize("T", [32768, 32769, 40000])
+def test_route_step_dispatch_at_tile_switch(T):
+    """The fused step's dispatch on either side of the tile-size switch: 128-token router tiles
+    (the dispatch counts the loads itself) and 256-token tiles with a ragged tail (the router
+    fills the loads table)."""
+    wl = datagen.WORKLOADS["large"].replace(T=T, d=256, seed=T + 3, n_clusters=8)
+    x, w, b = datagen.tokens(wl), datagen.router_weight(wl), datagen.initial_bias(wl)
+    step = elb.RouterStep(to_dev(w), to_dev(b), torch.zeros(wl.n_experts, device="cuda"), wl.k, T, update=False)
+    out = step(to_dev(x))
+    torch.cuda.synchronize()
+    idx = out.topk_idx.cpu().numpy()
+    check_counts(out.counts.cpu().numpy(), idx, wl.n_experts)
+    check_dispatch(out.offsets.cpu().numpy(), out.perm.cpu().numpy(), out.inv_perm.cpu().numpy(), idx, wl.n_experts)
+    log(f"T={T}: dispatch matches the oracle")

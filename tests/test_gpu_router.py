@@ -49,6 +49,23 @@ def test_router_matches_oracle(T, d, n_e, k, kind, kernel):
         f"gate rel err={rep.max_gate_rel:.2e} logit abs err={err:.2e}")
 
 
+@pytest.mark.parametrize("T", [
+    32767,   # 128-token tiles: 256 of them, ragged tail of 127
+    32768,   # the largest batch on 128-token tiles
+    32769,   # the smallest on 256-token tiles: 129 tiles, the last holding one token
+    40000,   # 256-token tiles with a ragged tail of 64
+])
+def test_router_tile_sizes(T):
+    """Both MFMA tile sizes and the switch between them, with ragged tails."""
+    log(f"router tile sizes T={T}")
+    wl, x, w, b = make(T, 256, 256, 4, kind="clusters")
+    idx, gates, counts, logits = run(x, w, b, 4)
+    rep = compare_route(idx, gates, x, w, b, 4)
+    check_counts(counts, idx, 256)
+    compare_logits(logits, x, w)
+    log(f"  ties={rep.ties} (mismatched {rep.tie_mismatch}) gate rel err={rep.max_gate_rel:.2e}")
+
+
 def test_fp32_tiny_workload():
     wl = datagen.WORKLOADS["tiny"]
     x, w, b = datagen.tokens(wl), datagen.router_weight(wl), datagen.initial_bias(wl)

@@ -163,9 +163,12 @@ def bench_next_rows(elb, wl, x, w, out, stream, reps: int = 20) -> dict:
     ws_b = torch.empty(elb.backward_workspace_bytes(T, d, n_e), dtype=torch.uint8, device=x.device)
     ms_b = time_events(lambda: elb.router_backward(x, w, out.topk_idx, dg, zloss_coef=1e-3, workspace=ws_b),
                        max(3, reps // 4), stream)
+    ms_b16 = time_events(lambda: elb.router_backward(x, w, out.topk_idx, dg, zloss_coef=1e-3, workspace=ws_b,
+                                                     dx_dtype=torch.bfloat16), max(3, reps // 4), stream)
     fl = 3 * 2.0 * T * n_e * d
-    res["backward"] = {"us": round(ms_b * 1e3, 2), "flops": fl, "tflops": round(fl / (ms_b * 1e-3) / 1e12, 1),
-                       "mfma_frac": round(fl / (ms_b * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    for name, ms in (("backward", ms_b), ("backward_bf16_dx", ms_b16)):
+        res[name] = {"us": round(ms * 1e3, 2), "flops": fl, "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                     "mfma_frac": round(fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
     esz = x.element_size()
     bytes_p = T * d * esz + T * k * d * esz + T * k * 4
     bytes_c = T * k * d * esz + T * k * 8 + T * d * 4

@@ -27,6 +27,7 @@ from ._lib import (  # noqa: F401
     ELB_ACCUMULATE_COUNTS,
     ELB_BF16,
     ELB_CLEAR_COUNTS,
+    ELB_DX_BF16,
     ELB_F32,
     ELB_FORCE_GENERIC,
     ELB_GATES_RAW,
@@ -253,9 +254,10 @@ def backward_workspace_bytes(T: int, d: int, n_experts: int) -> int:
 
 def router_backward(x: torch.Tensor, w: torch.Tensor, topk_idx: torch.Tensor, dgates: torch.Tensor, *,
                     gates_raw: bool = False, zloss_coef: float = 0.0, want_dx: bool = True, want_dw: bool = True,
-                    workspace: torch.Tensor | None = None):
+                    dx_dtype: torch.dtype = torch.float32, workspace: torch.Tensor | None = None):
     """Gradients of sum(dgates * gates) + zloss_coef * mean(lse^2) at the selection topk_idx:
-    returns (dx [T, d] fp32 or None, dw [N_r, d] fp32 or None).  bf16 x and w, d % 64 == 0."""
+    returns (dx [T, d] of dx_dtype (float32, or bfloat16 rounded to nearest even) or None,
+    dw [N_r, d] fp32 or None).  bf16 x and w, d % 64 == 0."""
     _need(x, "x", torch.bfloat16)
     dev = x.device
     _need(w, "w", torch.bfloat16, dev)
@@ -271,9 +273,12 @@ def router_backward(x: torch.Tensor, w: torch.Tensor, topk_idx: torch.Tensor, dg
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     else:
         _need(workspace, "workspace", device=dev)
-    dx = torch.empty((T, d), dtype=torch.float32, device=dev) if want_dx else None
+    if dx_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"dx_dtype must be float32 or bfloat16, got {dx_dtype}")
+    dx = torch.empty((T, d), dtype=dx_dtype, device=dev) if want_dx else None
     dw = torch.empty((n_e, d), dtype=torch.float32, device=dev) if want_dw else None
-    st = lib().elb_router_backward(_ptr(x), ELB_BF16, T, d, _ptr(w), n_e, k, ELB_GATES_RAW if gates_raw else 0,
+    flags = (ELB_GATES_RAW if gates_raw else 0) | (ELB_DX_BF16 if dx_dtype == torch.bfloat16 else 0)
+    st = lib().elb_router_backward(_ptr(x), ELB_BF16, T, d, _ptr(w), n_e, k, flags,
                                    _ptr(topk_idx), _ptr(dgates), float(zloss_coef), _ptr(dx), _ptr(dw),
                                    _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
     check("elb_router_backward", st)

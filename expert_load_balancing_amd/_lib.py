@@ -15,6 +15,7 @@ ELB_F32, ELB_BF16 = 0, 1
 ELB_MODE_SMEBU, ELB_MODE_SIGN, ELB_MODE_LINEAR = 0, 1, 2
 ELB_GATES_RAW, ELB_ACCUMULATE_COUNTS, ELB_FORCE_GENERIC = 1, 2, 4
 ELB_CLEAR_COUNTS = 1
+ELB_DX_BF16 = 8
 
 STATUS_NAMES = {0: "ELB_OK", 1: "ELB_ERR_NULL", 2: "ELB_ERR_SHAPE", 3: "ELB_ERR_UNSUPPORTED",
                 4: "ELB_ERR_ALIGN", 5: "ELB_ERR_WORKSPACE", 6: "ELB_ERR_LAUNCH"}

@@ -203,11 +203,11 @@ size_t elb_backward_workspace_bytes(int64_t T, int32_t d, int32_t n_experts) {
 
 elb_status elb_router_backward(const void* x, int32_t dtype, int64_t T, int32_t d, const void* w, int32_t n_experts,
                                int32_t k, uint32_t flags, const int32_t* topk_idx, const float* dgates,
-                               float zloss_coef, float* dx, float* dw, void* workspace, size_t workspace_bytes,
+                               float zloss_coef, void* dx, float* dw, void* workspace, size_t workspace_bytes,
                                elb_stream_t stream) {
   if (w == nullptr || workspace == nullptr) return ELB_ERR_NULL;
   if (T > 0 && (x == nullptr || topk_idx == nullptr || dgates == nullptr)) return ELB_ERR_NULL;
-  if (dtype != ELB_BF16 || (flags & ~(uint32_t)ELB_GATES_RAW)) return ELB_ERR_UNSUPPORTED;
+  if (dtype != ELB_BF16 || (flags & ~(uint32_t)(ELB_GATES_RAW | ELB_DX_BF16))) return ELB_ERR_UNSUPPORTED;
   if (T < 0 || T > (int64_t(1) << 22) || n_experts < 1 || n_experts > 256 || k < 1 || k > 8 || k > n_experts)
     return ELB_ERR_SHAPE;
   if (T * (int64_t)k >= (int64_t(1) << 31) || d < 1 || (int64_t)d * 2 * 256 >= (int64_t(1) << 30)) return ELB_ERR_SHAPE;
@@ -219,8 +219,8 @@ elb_status elb_router_backward(const void* x, int32_t dtype, int64_t T, int32_t 
   const elb::BackwardPlan plan = elb::backward_plan(T, d, workspace);
   if (workspace_bytes < plan.bytes) return ELB_ERR_WORKSPACE;
   if (dx == nullptr && dw == nullptr) return ELB_OK;
-  const elb::BackwardArgs a{x, T, d, w, n_experts, k, (flags & ELB_GATES_RAW) ? 0 : 1, topk_idx, dgates,
-                            zloss_coef, dx, dw};
+  const elb::BackwardArgs a{x,      T,          d,  w, n_experts, k, (flags & ELB_GATES_RAW) ? 0 : 1, topk_idx,
+                            dgates, zloss_coef, dx, (flags & ELB_DX_BF16) != 0, dw};
   return from_hip(elb::launch_router_backward(a, plan, reinterpret_cast<hipStream_t>(stream)));
 }
 

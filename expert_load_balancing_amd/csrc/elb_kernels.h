@@ -97,8 +97,9 @@ struct BackwardArgs {
   const int32_t* idx;
   const float* dgates;
   float zloss_coef;
-  float* dx;  // [T][d] fp32, or NULL
-  float* dw;  // [n_experts][d] fp32, or NULL
+  void* dx;      // [T][d] fp32 (bf16 with dx_bf16), or NULL
+  bool dx_bf16;
+  float* dw;     // [n_experts][d] fp32, or NULL
 };
 struct BackwardPlan {
   int64_t Q;        // 64-token stages of the batch

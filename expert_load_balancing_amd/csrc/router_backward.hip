@@ -51,17 +51,19 @@ __device__ __forceinline__ float sigmoid_fast(float z) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
 }
 
-constexpr int kDxStores = 16;  // stores per wave per dX stage: 64 tokens x 64 columns fp32, 1 KiB each
-static_assert(kDma + 2 * kDxStores <= 63, "vmcnt budget fits the counter");
+// Stores per wave per dX stage (64 tokens x 64 columns, 1 KiB each): 16 in fp32, 8 in bf16.
+template <bool DXBF>
+constexpr int kDxStores = DXBF ? 8 : 16;
+static_assert(kDma + 2 * kDxStores<false> <= 63, "vmcnt budget fits the counter");
 constexpr int kDxAhead = 3;  // k-blocks of W fragments read ahead (4 reads each, <= 15 in flight)
 
-// One 256-token tile: dZ [t][256] (bf16, token-major; NULL: not stored) and dX [t][d] (fp32;
-// NULL: not computed).  zc2 = 2 c / T (0: no z-loss term).
-template <int K, bool FULL>
+// One 256-token tile: dZ [t][256] (bf16, token-major; NULL: not stored) and dX [t][d] (fp32, or
+// bf16 rounded to nearest even with DXBF; NULL: not computed).  zc2 = 2 c / T (0: no z-loss).
+template <int K, bool FULL, bool DXBF>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void grad_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int64_t T, int d, int n_experts, int normalize,
     const int32_t* __restrict__ idx, const float* __restrict__ dgates, float zc2, uint16_t* __restrict__ dz,
-    float* __restrict__ dx) {
+    void* __restrict__ dx) {
   __shared__ __attribute__((aligned(1024))) unsigned char xs0[kSlot], xs1[kSlot], xs2[kSlot];
   __shared__ __attribute__((aligned(1024))) unsigned char ws0[kSlot], ws1[kSlot];
   const int tid = threadIdx.x;
@@ -204,7 +206,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // r + 2 in different halves of their window.  Store stage: xs2, 8 KiB a wave.
   //
   // vmcnt budget when stage j's DMAs must have landed: per stage a wave issues 8 DMAs (stage
-  // j + 2) and then kDxStores stores (stage j); behind stage j's DMAs come those of stage 1
+  // j + 2) and then kSt stores (stage j); behind stage j's DMAs come those of stage 1
   // (j = 0), the DMAs of stage 2 and the stores of stage 0 (j = 1), or the stores of j - 2, the
   // DMAs of j + 1 and the stores of j - 1 (j >= 2).  Stages 0 and 1 are peeled: one loop over
   // three different waits would leave the compiler's own wait analysis with the weakest.
@@ -229,14 +231,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // Stores go through a descriptor covering the tile's live rows: rows past T are dropped while
   // every store instruction still issues (the vmcnt budget counts them).  They are non-temporal:
   // with normal allocation the dX stream would push W out of L2, where every CU re-reads it.
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc(dx + row0 * d, (uint32_t)rows * (uint32_t)d * 4u);
+  constexpr int kEs = DXBF ? 2 : 4;  // bytes per dX element
+  constexpr int kSt = kDxStores<DXBF>;
+  const __amdgpu_buffer_rsrc_t xr =
+      make_rsrc(static_cast<unsigned char*>(dx) + row0 * d * kEs, (uint32_t)rows * (uint32_t)d * kEs);
   TrLane tl;
   tl.init(lane);
   const uint32_t ro = tl.row * (uint32_t)kRowB + tl.col;
   const uint32_t sw = ((tl.j >> 1) & 1u) << 6;  // ((row >> 1) & 1) << 2 chunks = 64 bytes
-  // Store q of a half: token rows wave*64 + 8 q + lane / 8, 16 bytes at column 4 (lane % 8).
-  const uint32_t so = (uint32_t)(wave * kRowsWave + (lane >> 3)) * (uint32_t)d * 4u + (uint32_t)(lane & 7) * 16u;
-  const uint32_t q_stride = 8u * (uint32_t)d * 4u;
+  // Store q: token rows wave*64 + 8 q + lane / 8, 16 bytes at byte 16 (lane % 8) of the row's
+  // 128-byte segment (fp32: of one 32-column half; bf16: of the whole 64-column stage).
+  const uint32_t so = (uint32_t)(wave * kRowsWave + (lane >> 3)) * (uint32_t)d * kEs + (uint32_t)(lane & 7) * 16u;
+  const uint32_t q_stride = 8u * (uint32_t)d * kEs;
   unsigned char* const stg = xs2 + wave * (kSlot / 4);
   // W fragment of k-block kb (experts 16 kb .. + 15), columns 32 cb .. + 31 of the stage.
   auto frag = [&](const unsigned char* sl, int kb, int cb) {
@@ -284,29 +290,50 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       if (kb + kDxAhead < 16) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
-    // Stores go out as whole 256-byte row segments, one 32-column half of the 64 x 64 fp32 tile
-    // at a time through the wave's LDS stage: [64 tokens][8 chunks of 16 bytes], chunk ch of
-    // token row t at ch ^ (t & 7).  Lane: token 32 nb + l32 of the wave; accumulator 4 g + r:
-    // column 32 cb + 8 g + 4 h + r of the stage, i.e. chunk 2 g + h of half cb.
-    const uint32_t ssoff = __builtin_amdgcn_readfirstlane((uint32_t)j * (kBK * 4));
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-#pragma unroll
-      for (int nb = 0; nb < kNB; ++nb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int t = nb * 32 + l32;
-          const f32x4 v = {c[cb][nb][4 * g], c[cb][nb][4 * g + 1], c[cb][nb][4 * g + 2], c[cb][nb][4 * g + 3]};
-          *reinterpret_cast<f32x4*>(stg + t * 128 + (((2 * g + h) ^ (t & 7)) << 4)) = v;
-        }
-      // Store q: tokens 8 q .. 8 q + 7, 8 lanes (8 chunks) per token row.
+    // Stores go out as whole 128-byte row segments through the wave's 8 KiB LDS stage,
+    // [64 tokens][8 chunks of 16 bytes], chunk ch of token row t at ch ^ (t & 7); fp32 takes one
+    // 32-column half of the 64 x 64 tile at a time, bf16 the whole tile.  Lane: token
+    // 32 nb + l32 of the wave; accumulator 4 g + r: column 32 cb + 8 g + 4 h + r of the stage.
+    const uint32_t ssoff = __builtin_amdgcn_readfirstlane((uint32_t)j * (kBK * kEs));
+    // Store q: tokens 8 q .. 8 q + 7, 8 lanes (8 chunks) per token row.
+    auto flush = [&](uint32_t seg) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const int t = 8 * q + (lane >> 3);
         const f32x4 v = *reinterpret_cast<const f32x4*>(stg + t * 128 + (((lane & 7) ^ (t & 7)) << 4));
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), xr,
-                                               (int)(so + (uint32_t)q * q_stride + (uint32_t)cb * 128u), (int)ssoff,
-                                               kAuxStream);
+                                               (int)(so + (uint32_t)q * q_stride + seg), (int)ssoff, kAuxStream);
+      }
+    };
+    if constexpr (DXBF) {
+      // Chunk of columns 32 cb + 8 g .. + 7 is 4 cb + g; the lane's 4 columns are its half h.
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int t = nb * 32 + l32;
+            const uint2 v = {bf16_rne(c[cb][nb][4 * g]) | (bf16_rne(c[cb][nb][4 * g + 1]) << 16),
+                             bf16_rne(c[cb][nb][4 * g + 2]) | (bf16_rne(c[cb][nb][4 * g + 3]) << 16)};
+            // One integer offset: split into two pointer steps, the compiler lost track of which
+            // LDS array the store hits and drained every DMA and store before it.
+            *reinterpret_cast<uint2*>(stg + (t * 128 + (((4 * cb + g) ^ (t & 7)) << 4) + 8 * h)) = v;
+          }
+      flush(0u);
+    } else {
+      // Chunk of columns 32 cb + 8 g + 4 h .. + 3 within half cb is 2 g + h.
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int t = nb * 32 + l32;
+            const f32x4 v = {c[cb][nb][4 * g], c[cb][nb][4 * g + 1], c[cb][nb][4 * g + 2], c[cb][nb][4 * g + 3]};
+            *reinterpret_cast<f32x4*>(stg + t * 128 + (((2 * g + h) ^ (t & 7)) << 4)) = v;
+          }
+        flush((uint32_t)cb * 128u);
       }
     }
   };
@@ -314,20 +341,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   bare_barrier();
   stage(0, xs0, ws0);
   if (nst > 1) {
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDma + kDxStores) & ~(15 << 8));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDma + kSt) & ~(15 << 8));
     bare_barrier();
     stage(1, xs1, xs0);
   }
   for (int j = 2; j < nst; j += 3) {
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDma + 2 * kDxStores) & ~(15 << 8));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDma + 2 * kSt) & ~(15 << 8));
     bare_barrier();
     stage(j, ws0, xs1);
     if (j + 1 >= nst) break;
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDma + 2 * kDxStores) & ~(15 << 8));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDma + 2 * kSt) & ~(15 << 8));
     bare_barrier();
     stage(j + 1, xs0, ws0);
     if (j + 2 >= nst) break;
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDma + 2 * kDxStores) & ~(15 << 8));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDma + 2 * kSt) & ~(15 << 8));
     bare_barrier();
     stage(j + 2, xs1, xs0);
   }
@@ -412,16 +439,21 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(const float4* __re
   }
 }
 
-template <int K>
-hipError_t launch_grad_k(const BackwardArgs& a, const BackwardPlan& p, hipStream_t s) {
+template <int K, bool DXBF>
+hipError_t launch_grad_kb(const BackwardArgs& a, const BackwardPlan& p, hipStream_t s) {
   const dim3 grid((unsigned)((a.T + kRowsB - 1) / kRowsB));
   const float zc2 = 2.0f * a.zloss_coef / (float)a.T;
   uint16_t* const dz = a.dw != nullptr ? p.dz : nullptr;
   if (a.n_experts == kRowsA)
-    return launch(grad_kernel<K, true>, grid, dim3(kThreads), 0, s, (const uint16_t*)a.x, (const uint16_t*)a.w, a.T,
-                  a.d, a.n_experts, a.normalize, a.idx, a.dgates, zc2, dz, a.dx);
-  return launch(grad_kernel<K, false>, grid, dim3(kThreads), 0, s, (const uint16_t*)a.x, (const uint16_t*)a.w, a.T,
-                a.d, a.n_experts, a.normalize, a.idx, a.dgates, zc2, dz, a.dx);
+    return launch(grad_kernel<K, true, DXBF>, grid, dim3(kThreads), 0, s, (const uint16_t*)a.x, (const uint16_t*)a.w,
+                  a.T, a.d, a.n_experts, a.normalize, a.idx, a.dgates, zc2, dz, a.dx);
+  return launch(grad_kernel<K, false, DXBF>, grid, dim3(kThreads), 0, s, (const uint16_t*)a.x, (const uint16_t*)a.w,
+                a.T, a.d, a.n_experts, a.normalize, a.idx, a.dgates, zc2, dz, a.dx);
+}
+
+template <int K>
+hipError_t launch_grad_k(const BackwardArgs& a, const BackwardPlan& p, hipStream_t s) {
+  return a.dx_bf16 ? launch_grad_kb<K, true>(a, p, s) : launch_grad_kb<K, false>(a, p, s);
 }
 
 }  // namespace

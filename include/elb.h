@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define ELB_VERSION 10400 /* major * 10000 + minor * 100 + patch */
+#define ELB_VERSION 10500 /* major * 10000 + minor * 100 + patch */
 
 typedef struct ihipStream_t* elb_stream_t; /* hipStream_t; NULL = default stream */
 
@@ -62,6 +62,11 @@ enum {
                                       overwriting them                                      */
   ELB_FORCE_GENERIC = 1u << 2      /* use the shape-generic kernel even where the MFMA
                                       kernel applies (tests compare the two)                 */
+};
+
+/* Flags of elb_router_backward (beside ELB_GATES_RAW). */
+enum {
+  ELB_DX_BF16 = 1u << 3 /* dx is written in bf16 (round to nearest even) instead of fp32 */
 };
 
 /* Flags of elb_balance_params. */
@@ -264,7 +269,8 @@ elb_status elb_unpermute_combine(const void* expert_out, int32_t dtype, int64_t 
  * section "Precision Fallbacks, Loss Stabilization, and MaxVio ..."):
  *   dL/dz_{t,i_j} = dL/ds_j s_j (1 - s_j),  dL/ds_j = (G_j - sum_m G_m g_m) / S (raw: G_j),
  *   dL/dz_{t,i}  += (2 zloss_coef / T) lse_t softmax(z_t)_i,
- *   dx = dL/dZ W [T, d] fp32,  dw = dL/dZ^T X [n_experts, d] fp32 (either may be NULL).
+ *   dx = dL/dZ W [T, d] fp32 (bf16 with ELB_DX_BF16, rounded to nearest even),
+ *   dw = dL/dZ^T X [n_experts, d] fp32 (either may be NULL).
  * The logits are recomputed from x and w on the matrix cores; dL/dz is rounded to bf16 before
  * the two products, which accumulate in fp32.
  *   x, w, topk_idx as in elb_router_forward (bf16 only, d % 64 == 0); dgates [T, k] fp32;
@@ -272,13 +278,13 @@ elb_status elb_unpermute_combine(const void* expert_out, int32_t dtype, int64_t 
  *   workspace: at least elb_backward_workspace_bytes(T, d, n_experts) bytes, 256-byte aligned;
  *   contents on entry do not matter.  topk_idx entries must lie in [0, n_experts).
  * Supported: 0 <= T <= 2^22, T * k < 2^31, 1 <= k <= min(8, n_experts), n_experts <= 256.
- * Errors: ELB_ERR_NULL, ELB_ERR_SHAPE, ELB_ERR_UNSUPPORTED (dtype, d % 64, flag), ELB_ERR_ALIGN,
- * ELB_ERR_WORKSPACE, ELB_ERR_LAUNCH.
+ * Errors: ELB_ERR_NULL, ELB_ERR_SHAPE, ELB_ERR_UNSUPPORTED (dtype, d % 64, flag other than
+ * ELB_GATES_RAW and ELB_DX_BF16), ELB_ERR_ALIGN, ELB_ERR_WORKSPACE, ELB_ERR_LAUNCH.
  */
 size_t elb_backward_workspace_bytes(int64_t T, int32_t d, int32_t n_experts);
 elb_status elb_router_backward(const void* x, int32_t dtype, int64_t T, int32_t d, const void* w, int32_t n_experts,
                                int32_t k, uint32_t flags, const int32_t* topk_idx, const float* dgates,
-                               float zloss_coef, float* dx, float* dw, void* workspace, size_t workspace_bytes,
+                               float zloss_coef, void* dx, float* dw, void* workspace, size_t workspace_bytes,
                                elb_stream_t stream);
 
 /*

@@ -35,6 +35,17 @@ def test_exports_every_declared_function(lib):
         assert getattr(lib, name) is not None
 
 
+def test_flag_constants_match_header():
+    """The binding's flag and enum constants are the header's values."""
+    text = open(HEADER).read()
+    found = {}
+    for name, val in re.findall(r"\b(ELB_[A-Z0-9_]+)\s*=\s*([0-9]+u?\s*<<\s*[0-9]+|[0-9]+)", text):
+        found[name] = eval(val.replace("u", ""))  # "1u << 3" or "5": plain integer arithmetic
+    for name in ("ELB_GATES_RAW", "ELB_ACCUMULATE_COUNTS", "ELB_FORCE_GENERIC", "ELB_CLEAR_COUNTS", "ELB_DX_BF16",
+                 "ELB_F32", "ELB_BF16", "ELB_MODE_SMEBU", "ELB_MODE_SIGN", "ELB_MODE_LINEAR"):
+        assert getattr(_lib, name) == found[name], name
+
+
 def test_version_matches_header(lib):
     m = re.search(r"#define ELB_VERSION (\d+)", open(HEADER).read())
     assert lib.elb_version() == int(m.group(1))
@@ -249,7 +260,8 @@ def test_backward_workspace_size(lib):
 
 @pytest.mark.parametrize("kw,want", [
     (dict(w=None), NULL), (dict(ws=None), NULL), (dict(x=None), NULL), (dict(idx=None), NULL), (dict(g=None), NULL),
-    (dict(dtype=0), UNSUPPORTED), (dict(flags=2), UNSUPPORTED), (dict(d=96), UNSUPPORTED),
+    (dict(dtype=0), UNSUPPORTED), (dict(flags=2), UNSUPPORTED), (dict(flags=8 | 4), UNSUPPORTED),
+    (dict(d=96), UNSUPPORTED),
     (dict(T=-1), SHAPE), (dict(T=(1 << 22) + 1), SHAPE), (dict(n=0), SHAPE), (dict(n=257), SHAPE), (dict(k=9), SHAPE),
     (dict(n=4, k=5), SHAPE), (dict(zc=float("nan")), SHAPE), (dict(zc=float("inf")), SHAPE),
     (dict(x=FAKE + 8), ALIGN), (dict(dw=FAKE + 4), ALIGN), (dict(dx=FAKE + 8), ALIGN), (dict(ws=FAKE + 64), ALIGN),

@@ -160,3 +160,20 @@ def test_backward_stress_size():
         mag += np.abs(d_).T @ np.abs(xc)
     r = check(dw, ref, (2.0 ** -8 + wl.T * 2.0 ** -24) * mag, "dw whole batch")
     log(f"  worst dw error / bound {r:.3f}")
+
+
+@pytest.mark.parametrize("T,d,n_e,k", [(700, 256, 256, 4), (2100, 192, 64, 4), (4113, 1088, 128, 2)])
+def test_backward_bf16_dx_is_rounded_fp32(T, d, n_e, k):
+    """With ELB_DX_BF16 the kernel runs the same fp32 accumulation and rounds at the store: dx in
+    bf16 is exactly the fp32 dx rounded to nearest even, and dw is unchanged."""
+    x, w, b = make(T, d, n_e, k, seed=T + 1)
+    xd, wd = to_dev(x), to_dev(w)
+    idx, _, _ = elb.router_forward(xd, wd, to_dev(b), k)
+    G = to_dev(np.random.default_rng(T).standard_normal((T, k)).astype(np.float32))
+    dx32, dw32 = elb.router_backward(xd, wd, idx, G, zloss_coef=0.05)
+    dx16, dw16 = elb.router_backward(xd, wd, idx, G, zloss_coef=0.05, dx_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert dx16.dtype == torch.bfloat16
+    assert torch.equal(dx16, dx32.to(torch.bfloat16))
+    assert torch.equal(dw16, dw32)
+    log(f"T={T} d={d}: bf16 dx == rne(fp32 dx)")

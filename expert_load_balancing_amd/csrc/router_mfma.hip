@@ -14,10 +14,11 @@
 //   One workgroup (4 waves, one per SIMD) owns a tile of 256 tokens x all 256 experts and
 //   keeps the 256x256 fp32 logit tile in registers (each wave: 256 experts x 64 tokens = 16
 //   accumulators of 32x32).  Batches of at most 128 x 256 tokens (one 256-token tile per CU
-//   would leave CUs idle) take 128-token tiles instead: each wave 256 experts x 32 tokens.  The contraction is written transposed, Z^T = W . X^T, so that the
-//   32x32 MFMA output puts one token per lane column: a lane ends up holding 128 of the 256
-//   logits of each of its tokens, and the other 128 sit in lane ^ 32.  Top-K therefore needs
-//   no LDS round trip: a register-local selection over 128 values, then one cross-lane merge.
+//   would leave CUs idle) take 128-token tiles instead: each wave 256 experts x 32 tokens.
+//   The contraction is written transposed, Z^T = W . X^T, so that the 32x32 MFMA output puts
+//   one token per lane column: a lane ends up holding 128 of the 256 logits of each of its
+//   tokens, and the other 128 sit in lane ^ 32.  Top-K therefore needs no LDS round trip: a
+//   register-local selection over 128 values, then one cross-lane merge.
 //
 // Memory pipeline: the product runs on the shared streaming tile of mfma_tile.hpp with
 //   A = the router weights (L2-resident, cached) and B = the tile's tokens (read once from HBM,

@@ -53,6 +53,8 @@ def check(got, ref, bound, what):
     (2100, 192, 64, 4, False, 0.0),   # d not a multiple of 256: one column tile, 33 token ranges
     (777, 320, 256, 4, True, 0.05),   # two column tiles, the second with 64 live columns
     (4113, 1088, 128, 2, False, 0.0),  # 5 column tiles -> 51 token ranges of 1-2 stages
+    (300, 8192, 256, 4, True, 0.02),   # wide rows: 32 column tiles, 128 W stages in the dX phase
+    (200, 128, 1, 1, True, 0.3),       # a single expert: the normalised gate is 1, dL/dz only the z-loss
 ])
 def test_backward_matches_oracle(T, d, n_e, k, normalize, zc):
     log(f"backward T={T} d={d} N_r={n_e} K={k} normalize={normalize} zloss={zc}")

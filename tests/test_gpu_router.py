@@ -36,6 +36,8 @@ def run(x, w, b, k, **kw):
     (450, 256, 200, 4, "iid"),         # padded experts (200 of 256)
     (129, 64, 16, 2, "iid"),           # tiny expert count, d = one stage
     (2048, 1024, 256, 4, "clusters"),
+    (300, 8192, 256, 4, "clusters"),   # wide rows: 16 KiB per token
+    (200, 128, 1, 1, "iid"),           # a single expert
 ])
 @pytest.mark.parametrize("kernel", ["mfma", "generic"])
 def test_router_matches_oracle(T, d, n_e, k, kind, kernel):

@@ -202,14 +202,20 @@ struct KRows {
 };
 
 // The streaming product.  AUX_A / AUX_B: cache policies of the two streams; LA / LB: their
-// layouts; NB: 32-row blocks of B per wave.  A's rows are `a_row_bytes` apart, B's
-// `b_row_bytes`; `nkb` stages of kBK elements are contracted (nkb >= 1).
-template <int AUX_A, int AUX_B, class LA = RowsK, class LB = RowsK, int NB = kNB>
+// layouts; NB: 32-row blocks of B per wave; ES: waves sharing one B row range, each with
+// 256 / ES of the A rows (ES = 2: 8 waves, two per SIMD, so that one wave's stalled DMA or LDS
+// read leaves the other issuing MFMAs).  Wave w owns A blocks (w % ES) * kMB / ES .. and B blocks
+// (w / ES) * NB ...  A's rows are `a_row_bytes` apart, B's `b_row_bytes`; `nkb` stages of kBK
+// elements are contracted (nkb >= 1).
+template <int AUX_A, int AUX_B, class LA = RowsK, class LB = RowsK, int NB = kNB, int ES = 1>
 struct Stream {
   static_assert(NB == kNB || (NB == 1 && LB::kReads == 1), "a 128-row B tile is laid out rows-contiguous-in-k");
-  // DMA instructions per wave per stage (1 KiB each): A's 256 rows, B's 128 NB rows, over 4 waves.
-  static constexpr int kDmaA = kDma;
-  static constexpr int kDmaB = kDma * NB / kNB;
+  static_assert(ES == 1 || (ES == 2 && LA::kReads == 1 && LB::kReads == 1), "the 8-wave split: rows-contiguous-in-k");
+  static constexpr int kWavesS = kWaves * ES;
+  static constexpr int kMBw = kMB / ES;  // A blocks per wave
+  // DMA instructions per wave per stage (1 KiB each): A's 256 rows, B's 128 NB rows, over the waves.
+  static constexpr int kDmaA = kDma / ES;
+  static constexpr int kDmaB = kDma * NB / kNB / ES;
   // VMEM instructions a wave issues after the DMAs of stage j's A rows, when it must have stage
   // j: the B DMAs of the same iteration, then (kPW - 1) full iterations.
   static constexpr int kBudget = kDmaB + (kDmaA + kDmaB) * (kPW - 1);
@@ -229,9 +235,9 @@ struct Stream {
     nkb = n_stages;
     sl = slots;
 #pragma unroll
-    for (int i = 0; i < kDmaA; ++i) voa[i] = LA::dma_off(wave, lane, i, a_row_bytes, 64);
+    for (int i = 0; i < kDmaA; ++i) voa[i] = LA::dma_off(wave, lane, i, a_row_bytes, 64 / ES);
 #pragma unroll
-    for (int i = 0; i < kDmaB; ++i) vob[i] = LB::dma_off(wave, lane, i, b_row_bytes, 32 * NB);
+    for (int i = 0; i < kDmaB; ++i) vob[i] = LB::dma_off(wave, lane, i, b_row_bytes, 32 * NB / ES);
     wave_off_a = (uint32_t)wave * (kDmaA * 1024);  // A: 64 rows x 128 B or 16 rows x 512 B
     wave_off_b = (uint32_t)wave * (kDmaB * 1024);
     a_stage = LA::stage_bytes(a_row_bytes);
@@ -253,18 +259,20 @@ struct Stream {
 
   // acc <- the product over all nkb stages (after prologue()).  On return every DMA has landed
   // and every wave is past its last operand read (the slots may be reused).
-  __device__ __forceinline__ void run(f32x16 (&acc)[kMB][NB], int wave, int lane) {
+  __device__ __forceinline__ void run(f32x16 (&acc)[kMBw][NB], int wave, int lane) {
     typename LA::Lane la;
     typename LB::Lane lb;
     la.init(lane);
     lb.init(lane);
 
 #pragma unroll
-    for (int mb = 0; mb < kMB; ++mb)
+    for (int mb = 0; mb < kMBw; ++mb)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
+    const int ea = (wave % ES) * kMBw;  // first A block of the wave
+    const int tb = (wave / ES) * NB;    // first B block of the wave
 
     // nkb >= 1 always: a do-while tells the compiler so, and spares it a second, never-run copy
     // of the 256 zero accumulators held across the loop.
@@ -291,12 +299,12 @@ struct Stream {
         // Operand fragments are double-buffered: the LDS reads of k-step s + 1 go out before
         // the 16 MFMAs of k-step s, so their latency hides behind 512 MFMA cycles (one wave per
         // SIMD has no other wave to hide it).
-        bf16x8 a[2][kMB], b[2][NB];
+        bf16x8 a[2][kMBw], b[2][NB];
         auto fetch = [&](int buf, int s) {
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) b[buf][nb] = lb.frag(xs, wave * NB + nb, s);
+          for (int nb = 0; nb < NB; ++nb) b[buf][nb] = lb.frag(xs, tb + nb, s);
 #pragma unroll
-          for (int mb = 0; mb < kMB; ++mb) a[buf][mb] = la.frag(ws, mb, s);
+          for (int mb = 0; mb < kMBw; ++mb) a[buf][mb] = la.frag(ws, ea + mb, s);
         };
         fetch(0, 0);
         fetch(1, 1);
@@ -304,17 +312,17 @@ struct Stream {
         for (int s = 0; s < kKSteps; ++s) {
           if (s >= 1 && s + 1 < kKSteps) fetch((s + 1) & 1, s + 1);
 #pragma unroll
-          for (int mb = 0; mb < kMB; ++mb)
+          for (int mb = 0; mb < kMBw; ++mb)
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
               acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][mb], b[s & 1][nb], acc[mb][nb], 0, 0, 0);
         }
         // Issue order for the scheduler: reads of steps 0 and 1; then per step its MFMAs with
         // kDma / kKSteps B DMAs slotted between them, and the reads of step s + 2.
-        static_assert(kDmaB % kKSteps == 0 && (kMB * NB) % (kDmaB / kKSteps) == 0, "DMA interleave");
+        static_assert(kDmaB % kKSteps == 0 && (kMBw * NB) % (kDmaB / kKSteps) == 0, "DMA interleave");
         constexpr int kDmaPerStep = kDmaB / kKSteps;
-        constexpr int kMfmaPerDma = kMB * NB / kDmaPerStep;
-        constexpr int kReadsStep = kMB * LA::kReads + NB * LB::kReads;
+        constexpr int kMfmaPerDma = kMBw * NB / kDmaPerStep;
+        constexpr int kReadsStep = kMBw * LA::kReads + NB * LB::kReads;
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * kReadsStep, 0);  // DS reads, steps 0 and 1
 #pragma unroll
         for (int s = 0; s < kKSteps; ++s) {

@@ -61,9 +61,175 @@ __device__ __forceinline__ float sigmoid_fast(float z) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
 }
 
-// NB: 32-token blocks per wave (tile of 128 NB tokens).
+// Epilogue of the 8-wave tile (ES = 2).  Wave w holds experts 128 eh .. + 127 (eh = w % 2) of
+// tokens 32 NB tq .. (tq = w / 2); a lane holds 64 of them for its token, lane ^ 32 the other 64.
+// Per 32-token block: every wave selects its K best (same keys as the 4-wave epilogue, a
+// lane-local slot in the low bits, re-keyed with 255 - expert before the merges), parks its
+// scores, and leaves its K keys (and, with EXTRA, its log-sum-exp partial) in LDS; after a
+// barrier one wave of each pair (eh = block parity) merges the partner's K keys and writes the
+// token's indices, gates and histogram counts.  b' (the shifted bias) is in ws1[0..1 KiB), the
+// histogram in ws1[1..2 KiB).
 template <int K, bool FULL, bool EXTRA, int NB>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void router_mfma_kernel(
+__device__ __forceinline__ void epilogue_split(const f32x16 (&acc)[kMB / 2][NB], int tid, int wave, int lane,
+                                               int64_t row0, int64_t T, int n_experts, int normalize, float bshift,
+                                               unsigned char* xs0, unsigned char* xs1, unsigned char* xs2,
+                                               unsigned char* ws0, unsigned char* ws1, int32_t* __restrict__ idx_out,
+                                               float* __restrict__ gates_out, float* __restrict__ logits,
+                                               float* __restrict__ lse) {
+  constexpr int kMBw = kMB / 2;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+  const int eh = wave & 1, tq = wave >> 1;
+  float* const bprime = reinterpret_cast<float*>(ws1);
+  int* const hist = reinterpret_cast<int*>(ws1 + 1024);
+  float* const xkey = reinterpret_cast<float*>(ws1 + 2048);                   // [8 waves][32 tokens][8]
+  float2* const xlse = reinterpret_cast<float2*>(ws1 + 2048 + 8 * 32 * 8 * 4);  // [8 waves][32 tokens]
+  if (tid < kExp) {
+    bprime[tid] = tid < n_experts ? bshift : 0.0f;
+    hist[tid] = 0;
+  }
+  // Parks: wave v's scores in the 16 KiB half (v & 1) of slot v / 2, [16 groups][64 lanes][4].
+  auto park_of = [&](int v) {
+    unsigned char* const sl = (v >> 1) == 0 ? xs0 : (v >> 1) == 1 ? xs1 : (v >> 1) == 2 ? xs2 : ws0;
+    return reinterpret_cast<float*>(sl + (v & 1) * 16384);
+  };
+  float* const park = park_of(wave);
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  bare_barrier();
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int64_t t = row0 + tq * (32 * NB) + nb * 32 + l32;
+    float top[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) top[j] = 0.0f;
+#pragma unroll
+    for (int mb = 0; mb < kMBw; ++mb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int e0 = 128 * eh + mb * 32 + g * 8 + 4 * h;
+        const f32x4 bp = *reinterpret_cast<const f32x4*>(bprime + e0);
+        f32x4 sv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float sc = sigmoid_fast(acc[mb][nb][g * 4 + r]);
+          sv[r] = sc;
+          const uint32_t slot_id = (uint32_t)(63 - (mb * 16 + g * 4 + r));  // lane-local, ascending expert
+          const float key = __uint_as_float((__float_as_uint(sc + bp[r]) & 0xFFFFFF00u) | slot_id);
+          topk_insert<K>(top, FULL || e0 + r < n_experts ? key : 0.0f);
+        }
+        *reinterpret_cast<f32x4*>(park + ((mb * 4 + g) * 64 + lane) * 4) = sv;
+      }
+    }
+    // Re-key with the global expert id, merge with lane ^ 32 (the wave's other 64 experts).
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const uint32_t bits = __float_as_uint(top[j]);
+      const int ls = 63 - (int)(bits & 0x3Fu);
+      const int e = 128 * eh + (((ls >> 2) << 3) | (h << 2) | (ls & 3));
+      top[j] = __uint_as_float((bits & 0xFFFFFF00u) | (uint32_t)(255 - e));
+    }
+    float other[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) other[j] = __shfl_xor(top[j], 32);
+#pragma unroll
+    for (int j = 0; j < K; ++j) topk_insert<K>(top, other[j]);
+    if (h == 0) {
+#pragma unroll
+      for (int j = 0; j < K; ++j) xkey[(wave * 32 + l32) * 8 + j] = top[j];
+    }
+    float m = -__builtin_inff(), sum = 0.0f;
+    if constexpr (EXTRA) {
+      if (logits != nullptr && t < T) {
+#pragma unroll
+        for (int mb = 0; mb < kMBw; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int ee = 128 * eh + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (ee < n_experts) logits[t * n_experts + ee] = acc[mb][nb][r];
+          }
+      }
+      if (lse != nullptr) {
+        // This wave's partial over its 128 experts (the lane's 64 merged with lane ^ 32's).
+#pragma unroll
+        for (int mb = 0; mb < kMBw; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int ee = 128 * eh + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (ee < n_experts) m = fmaxf(m, acc[mb][nb][r]);
+          }
+#pragma unroll
+        for (int mb = 0; mb < kMBw; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int ee = 128 * eh + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (ee < n_experts) sum += __builtin_amdgcn_exp2f((acc[mb][nb][r] - m) * kLog2e);
+          }
+        const float m2 = __shfl_xor(m, 32);
+        const float sum2 = __shfl_xor(sum, 32);
+        const float mm = fmaxf(m, m2);
+        // An empty half (every expert past n_experts) has m = -inf and contributes nothing.
+        sum = (m == mm ? sum : sum * __builtin_amdgcn_exp2f((m - mm) * kLog2e)) +
+              (m2 == mm ? sum2 : sum2 * __builtin_amdgcn_exp2f((m2 - mm) * kLog2e));
+        m = mm;
+        if (h == 0) xlse[wave * 32 + l32] = float2{m, sum};
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    bare_barrier();  // parks, keys and partials of every wave are visible
+    if (eh == (nb & 1)) {
+      const int partner = wave ^ 1;
+#pragma unroll
+      for (int j = 0; j < K; ++j) topk_insert<K>(top, xkey[(partner * 32 + l32) * 8 + j]);
+      if (t < T) {
+        int e[K];
+        float sg[K];
+        float ssum = 0.0f;
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+          e[j] = 255 - (int)(__float_as_uint(top[j]) & 0xFFu);
+          const int el = e[j] & 127;
+          const float* const pk = park_of(2 * tq + (e[j] >> 7));
+          sg[j] = pk[(((el >> 5) * 4 + ((el & 31) >> 3)) * 64 + l32 + 32 * ((el >> 2) & 1)) * 4 + (el & 3)];
+          ssum += sg[j];
+        }
+        if (h == 0) {
+          if constexpr (K == 4) {
+            *reinterpret_cast<i32x4*>(idx_out + t * 4) = i32x4{e[0], e[1], e[2], e[3]};
+          } else {
+#pragma unroll
+            for (int j = 0; j < K; ++j) idx_out[t * K + j] = e[j];
+          }
+#pragma unroll
+          for (int j = 0; j < K; ++j) atomicAdd(&hist[e[j]], 1);
+        } else {
+          const float inv = normalize ? 1.0f / ssum : 1.0f;
+          if constexpr (K == 4) {
+            *reinterpret_cast<f32x4*>(gates_out + t * 4) = f32x4{sg[0] * inv, sg[1] * inv, sg[2] * inv, sg[3] * inv};
+          } else {
+#pragma unroll
+            for (int j = 0; j < K; ++j) gates_out[t * K + j] = sg[j] * inv;
+          }
+        }
+        if constexpr (EXTRA) {
+          if (lse != nullptr && h == 0) {
+            const float2 o = xlse[partner * 32 + l32];
+            const float mm = fmaxf(m, o.x);
+            const float tot = (m == mm ? sum : sum * __builtin_amdgcn_exp2f((m - mm) * kLog2e)) +
+                              (o.x == mm ? o.y : o.y * __builtin_amdgcn_exp2f((o.x - mm) * kLog2e));
+            lse[t] = mm + __logf(tot);
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    bare_barrier();  // the parks and keys are read before the next block overwrites them
+  }
+}
+
+// NB: 32-token blocks per wave (tile of 128 NB tokens).  ES: waves per token range (1: 4 waves,
+// each with all 256 experts; 2: 8 waves, two per SIMD, each with 128 experts).
+template <int K, bool FULL, bool EXTRA, int NB, int ES>
+__global__ __launch_bounds__(kThreads * ES) __attribute__((amdgpu_waves_per_eu(ES, ES))) void router_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const float* __restrict__ bias, int64_t T, int d,
     int n_experts, int normalize, int32_t* __restrict__ idx_out, float* __restrict__ gates_out,
     int32_t* __restrict__ counts, float* __restrict__ logits, float* __restrict__ lse,
@@ -90,7 +256,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
   // ---- operand streams: start the DMA ring (A = weights, B = this tile's tokens) ----
   const uint32_t row_bytes = (uint32_t)d * 2u;
-  Stream<kAuxCached, kAuxStream, RowsK, RowsK, NB> st;
+  Stream<kAuxCached, kAuxStream, RowsK, RowsK, NB, ES> st;
   st.init(w, (uint32_t)n_experts * row_bytes, row_bytes, x + row0 * d, (uint32_t)rows * row_bytes, row_bytes,
           d / kBK, wave, lane, Slots{xs0, xs1, xs2, ws0, ws1});
   st.prologue();
@@ -102,8 +268,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const float shift = 1.0f - mn;  // identical in every wave: min is exact
   const float bv = tid < n_experts ? bias[tid] : 0.0f;
 
-  f32x16 acc[kMB][NB];
+  f32x16 acc[kMB / ES][NB];
   st.run(acc, wave, lane);
+  if constexpr (ES == 1) {
 
   // ---- epilogue ----
   // The ring has drained: slot ws1 holds b' and the load histogram, and each wave parks its
@@ -225,6 +392,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     }
   }
 
+  } else {
+    epilogue_split<K, FULL, EXTRA, NB>(acc, tid, wave, lane, row0, T, n_experts, normalize, bv + shift, xs0, xs1, xs2,
+                                       ws0, ws1, idx_out, gates_out, logits, lse);
+  }
+
+  int* const hist = reinterpret_cast<int*>(ws1 + 1024);
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   bare_barrier();
   if (tid < n_experts) {
@@ -242,13 +415,14 @@ hipError_t launch_kfn(const RouterArgs& a, hipStream_t stream) {
   constexpr int kTok = 4 * 32 * NB;
   const dim3 grid((unsigned)((a.T + kTok - 1) / kTok));
   int32_t* const loads = NB == kNB ? a.tile_loads : nullptr;
+  constexpr int ES = NB == kNB ? 2 : 1;  // the full tile on 8 waves, the half tile on 4
   if (a.logits != nullptr || a.lse != nullptr)
-    return launch(router_mfma_kernel<K, FULL, true, NB>, grid, dim3(kThreads), 0, stream, (const uint16_t*)a.x,
-                  (const uint16_t*)a.w, a.bias, a.T, a.d, a.n_experts, normalize, a.idx, a.gates, a.counts,
-                  a.logits, a.lse, loads, a.loads_stride);
-  return launch(router_mfma_kernel<K, FULL, false, NB>, grid, dim3(kThreads), 0, stream, (const uint16_t*)a.x,
-                (const uint16_t*)a.w, a.bias, a.T, a.d, a.n_experts, normalize, a.idx, a.gates, a.counts,
-                a.logits, a.lse, loads, a.loads_stride);
+    return launch(router_mfma_kernel<K, FULL, true, NB, ES>, grid, dim3(kThreads * ES), 0, stream,
+                  (const uint16_t*)a.x, (const uint16_t*)a.w, a.bias, a.T, a.d, a.n_experts, normalize, a.idx,
+                  a.gates, a.counts, a.logits, a.lse, loads, a.loads_stride);
+  return launch(router_mfma_kernel<K, FULL, false, NB, ES>, grid, dim3(kThreads * ES), 0, stream,
+                (const uint16_t*)a.x, (const uint16_t*)a.w, a.bias, a.T, a.d, a.n_experts, normalize, a.idx,
+                a.gates, a.counts, a.logits, a.lse, loads, a.loads_stride);
 }
 
 template <int K, bool FULL>

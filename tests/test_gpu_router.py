@@ -68,6 +68,22 @@ def test_router_tile_sizes(T):
     log(f"  ties={rep.ties} (mismatched {rep.tie_mismatch}) gate rel err={rep.max_gate_rel:.2e}")
 
 
+@pytest.mark.parametrize("T,n_e,k", [(33000, 200, 8), (40000, 64, 1), (36000, 256, 3)])
+def test_router_full_tile_shapes(T, n_e, k):
+    """The full (8-wave) tile with padded experts (some waves hold none), every K, and the
+    log-sum-exp combined across the two waves of a token."""
+    log(f"router full tile T={T} N_r={n_e} K={k}")
+    wl, x, w, b = make(T, 128, n_e, k, kind="clusters")
+    res = elb.router_forward(to_dev(x), to_dev(w), to_dev(b), k, want_logits=True, want_lse=True)
+    torch.cuda.synchronize()
+    idx, gates, counts, logits, lse = [t.cpu().numpy() for t in res]
+    compare_route(idx, gates, x, w, b, k)
+    check_counts(counts, idx, n_e)
+    compare_logits(logits, x, w)
+    _, want = oracle.router_z_loss(oracle.router_logits(x, w))
+    assert np.allclose(lse.astype(np.float64), want, rtol=1e-5, atol=1e-5), np.abs(lse - want).max()
+
+
 def test_fp32_tiny_workload():
     wl = datagen.WORKLOADS["tiny"]
     x, w, b = datagen.tokens(wl), datagen.router_weight(wl), datagen.initial_bias(wl)

@@ -9,7 +9,9 @@
 //
 // Work decomposition: 4 waves, one per SIMD; wave w owns B rows 32 NB w .. + 32 NB - 1 against
 // all 256 A rows, i.e. 8 x NB accumulators of 32 x 32 (NB = 2: a 256 x 256 tile in 256 AGPRs;
-// NB = 1: a 256 x 128 tile, for batches too small to give every CU a 256-row B tile).  A 32 x 32 MFMA output puts one
+// NB = 1: a 256 x 128 tile, for batches too small to give every CU a 256-row B tile).  With
+// ES = 2 the workgroup has 8 waves, two per SIMD, and the waves 2 p and 2 p + 1 split those B
+// rows' A rows between them (128 each).  A 32 x 32 MFMA output puts one
 // B row per lane column: lane l holds column l % 32 of its block, and accumulator r holds A row
 // 8 (r / 4) + 4 (l / 32) + (r % 4).
 //
@@ -319,17 +321,24 @@ struct Stream {
         }
         // Issue order for the scheduler: reads of steps 0 and 1; then per step its MFMAs with
         // kDma / kKSteps B DMAs slotted between them, and the reads of step s + 2.
-        static_assert(kDmaB % kKSteps == 0 && (kMBw * NB) % (kDmaB / kKSteps) == 0, "DMA interleave");
-        constexpr int kDmaPerStep = kDmaB / kKSteps;
-        constexpr int kMfmaPerDma = kMBw * NB / kDmaPerStep;
+        // One B DMA after every kMfmaPerDma MFMAs: several per k-step, or one every few k-steps.
+        constexpr int kMfmaStage = kKSteps * kMBw * NB;
+        static_assert(kMfmaStage % kDmaB == 0 && ((kMfmaStage / kDmaB) % (kMBw * NB) == 0 ||
+                                                  (kMBw * NB) % (kMfmaStage / kDmaB) == 0), "DMA interleave");
+        constexpr int kMfmaPerDma = kMfmaStage / kDmaB;
         constexpr int kReadsStep = kMBw * LA::kReads + NB * LB::kReads;
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * kReadsStep, 0);  // DS reads, steps 0 and 1
 #pragma unroll
         for (int s = 0; s < kKSteps; ++s) {
+          if constexpr (kMfmaPerDma <= kMBw * NB) {
 #pragma unroll
-          for (int q = 0; q < kDmaPerStep; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerDma, 0);  // MFMAs, step s
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);            // one B DMA
+            for (int q = 0; q < kMBw * NB / kMfmaPerDma; ++q) {
+              __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerDma, 0);  // MFMAs, step s
+              __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);            // one B DMA
+            }
+          } else {
+            __builtin_amdgcn_sched_group_barrier(0x008, kMBw * NB, 0);  // MFMAs, step s
+            if ((s + 1) % (kMfmaPerDma / (kMBw * NB)) == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
           }
           if (s + 2 < kKSteps) __builtin_amdgcn_sched_group_barrier(0x100, kReadsStep, 0);  // DS reads, step s + 2
         }

@@ -11,14 +11,17 @@
 // No logit is written to memory unless the caller asks for the debug copy.
 //
 // Work decomposition
-//   One workgroup (4 waves, one per SIMD) owns a tile of 256 tokens x all 256 experts and
-//   keeps the 256x256 fp32 logit tile in registers (each wave: 256 experts x 64 tokens = 16
-//   accumulators of 32x32).  Batches of at most 128 x 256 tokens (one 256-token tile per CU
-//   would leave CUs idle) take 128-token tiles instead: each wave 256 experts x 32 tokens.
+//   One workgroup (8 waves, two per SIMD) owns a tile of 256 tokens x all 256 experts and
+//   keeps the 256x256 fp32 logit tile in registers: each wave pair shares 64 tokens, and each
+//   wave of the pair holds 128 of the experts (8 accumulators of 32x32).  Batches of at most
+//   128 x 256 tokens (one 256-token tile per CU would leave CUs idle) take 128-token tiles
+//   instead: each wave pair 32 tokens.  Two waves per SIMD let one wave's LDS reads and
+//   selection run under the other's MFMAs.
 //   The contraction is written transposed, Z^T = W . X^T, so that the 32x32 MFMA output puts
-//   one token per lane column: a lane ends up holding 128 of the 256 logits of each of its
-//   tokens, and the other 128 sit in lane ^ 32.  Top-K therefore needs no LDS round trip: a
-//   register-local selection over 128 values, then one cross-lane merge.
+//   one token per lane column: a lane ends up holding 64 of its wave's 128 logits of each of
+//   its tokens, and the other 64 sit in lane ^ 32.  Top-K needs only a small LDS exchange: a
+//   register-local selection over 64 values, one cross-lane merge, then the K best of the
+//   partner wave through LDS.
 //
 // Memory pipeline: the product runs on the shared streaming tile of mfma_tile.hpp with
 //   A = the router weights (L2-resident, cached) and B = the tile's tokens (read once from HBM,
@@ -61,7 +64,7 @@ __device__ __forceinline__ float sigmoid_fast(float z) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
 }
 
-// Epilogue of the 8-wave tile (ES = 2).  Wave w holds experts 128 eh .. + 127 (eh = w % 2) of
+// Epilogue of the 8-wave tile.  Wave w holds experts 128 eh .. + 127 (eh = w % 2) of
 // tokens 32 NB tq .. (tq = w / 2); a lane holds 64 of them for its token, lane ^ 32 the other 64.
 // Per 32-token block: every wave selects its K best (same keys as the 4-wave epilogue, a
 // lane-local slot in the low bits, re-keyed with 255 - expert before the merges), parks its
@@ -226,10 +229,10 @@ __device__ __forceinline__ void epilogue_split(const f32x16 (&acc)[kMB / 2][NB],
   }
 }
 
-// NB: 32-token blocks per wave (tile of 128 NB tokens).  ES: waves per token range (1: 4 waves,
-// each with all 256 experts; 2: 8 waves, two per SIMD, each with 128 experts).
-template <int K, bool FULL, bool EXTRA, int NB, int ES>
-__global__ __launch_bounds__(kThreads * ES) __attribute__((amdgpu_waves_per_eu(ES, ES))) void router_mfma_kernel(
+// NB: 32-token blocks per wave pair (tile of 128 NB tokens).  8 waves, two per SIMD: each pair
+// shares a token range, and each wave of it holds 128 of the 256 experts.
+template <int K, bool FULL, bool EXTRA, int NB>
+__global__ __launch_bounds__(kThreads * 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void router_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const float* __restrict__ bias, int64_t T, int d,
     int n_experts, int normalize, int32_t* __restrict__ idx_out, float* __restrict__ gates_out,
     int32_t* __restrict__ counts, float* __restrict__ logits, float* __restrict__ lse,
@@ -241,10 +244,7 @@ __global__ __launch_bounds__(kThreads * ES) __attribute__((amdgpu_waves_per_eu(E
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps LDS bases in SGPRs
-  const int h = lane >> 5;
-  const int l32 = lane & 31;
   constexpr int kTok = 4 * 32 * NB;  // tokens per workgroup
-  constexpr int kTokWave = 32 * NB;
   const int64_t row0 = (int64_t)blockIdx.x * kTok;
   const int rows = (int)(T - row0 < kTok ? T - row0 : kTok);
 
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(kThreads * ES) __attribute__((amdgpu_waves_per_eu(E
 
   // ---- operand streams: start the DMA ring (A = weights, B = this tile's tokens) ----
   const uint32_t row_bytes = (uint32_t)d * 2u;
-  Stream<kAuxCached, kAuxStream, RowsK, RowsK, NB, ES> st;
+  Stream<kAuxCached, kAuxStream, RowsK, RowsK, NB, 2> st;
   st.init(w, (uint32_t)n_experts * row_bytes, row_bytes, x + row0 * d, (uint32_t)rows * row_bytes, row_bytes,
           d / kBK, wave, lane, Slots{xs0, xs1, xs2, ws0, ws1});
   st.prologue();
@@ -268,134 +268,10 @@ __global__ __launch_bounds__(kThreads * ES) __attribute__((amdgpu_waves_per_eu(E
   const float shift = 1.0f - mn;  // identical in every wave: min is exact
   const float bv = tid < n_experts ? bias[tid] : 0.0f;
 
-  f32x16 acc[kMB / ES][NB];
+  f32x16 acc[kMB / 2][NB];
   st.run(acc, wave, lane);
-  if constexpr (ES == 1) {
-
-  // ---- epilogue ----
-  // The ring has drained: slot ws1 holds b' and the load histogram, and each wave parks its
-  // scores in a slot of its own: [32 row groups][64 lanes][4 floats].
-  float* const bprime = reinterpret_cast<float*>(ws1);
-  int* const hist = reinterpret_cast<int*>(ws1 + 1024);
-  bprime[tid] = tid < n_experts ? bv + shift : 0.0f;
-  hist[tid] = 0;
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-  bare_barrier();
-  float* const park = reinterpret_cast<float*>(wave == 0 ? xs0 : wave == 1 ? xs1 : wave == 2 ? xs2 : ws0);
-  // Output layout of a 32x32 MFMA block (rows = experts, columns = tokens): lane column l32 is
-  // the token; accumulator r holds expert row 8 (r / 4) + 4 h + (r % 4).
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int64_t t = row0 + wave * kTokWave + nb * 32 + l32;
-    float top[K];
-#pragma unroll
-    for (int j = 0; j < K; ++j) top[j] = 0.0f;
-#pragma unroll
-    for (int mb = 0; mb < kMB; ++mb) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int e0 = mb * 32 + g * 8 + 4 * h;
-        const f32x4 bp = *reinterpret_cast<const f32x4*>(bprime + e0);
-        f32x4 sv;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float s = sigmoid_fast(acc[mb][nb][g * 4 + r]);
-          sv[r] = s;
-          const uint32_t slot_id = (uint32_t)(127 - (mb * 16 + g * 4 + r));  // lane-local, ascending expert
-          const float key = __uint_as_float((__float_as_uint(s + bp[r]) & 0xFFFFFF00u) | slot_id);
-          topk_insert<K>(top, FULL || e0 + r < n_experts ? key : 0.0f);
-        }
-        *reinterpret_cast<f32x4*>(park + ((mb * 4 + g) * 64 + lane) * 4) = sv;
-      }
-    }
-    // Re-key the survivors with the global expert id, then merge with lane ^ 32, which holds
-    // the other 128 experts of the same token.
-    int e[K];
-#pragma unroll
-    for (int j = 0; j < K; ++j) {
-      const uint32_t bits = __float_as_uint(top[j]);
-      const int ls = 127 - (int)(bits & 0x7Fu);
-      e[j] = ((ls >> 2) << 3) | (h << 2) | (ls & 3);
-      top[j] = __uint_as_float((bits & 0xFFFFFF00u) | (uint32_t)(255 - e[j]));
-    }
-    float other[K];
-#pragma unroll
-    for (int j = 0; j < K; ++j) other[j] = __shfl_xor(top[j], 32);
-#pragma unroll
-    for (int j = 0; j < K; ++j) topk_insert<K>(top, other[j]);
-    wave_lds_sync();
-
-    if (t < T) {
-      float sg[K];
-      float ssum = 0.0f;
-#pragma unroll
-      for (int j = 0; j < K; ++j) {
-        e[j] = 255 - (int)(__float_as_uint(top[j]) & 0xFFu);
-        const int src_lane = l32 + 32 * ((e[j] >> 2) & 1);
-        sg[j] = park[((e[j] >> 3) * 64 + src_lane) * 4 + (e[j] & 3)];
-        ssum += sg[j];
-      }
-      if (h == 0) {
-        if constexpr (K == 4) {
-          *reinterpret_cast<i32x4*>(idx_out + t * 4) = i32x4{e[0], e[1], e[2], e[3]};
-        } else {
-#pragma unroll
-          for (int j = 0; j < K; ++j) idx_out[t * K + j] = e[j];
-        }
-#pragma unroll
-        for (int j = 0; j < K; ++j) atomicAdd(&hist[e[j]], 1);
-      } else {
-        const float inv = normalize ? 1.0f / ssum : 1.0f;
-        if constexpr (K == 4) {
-          *reinterpret_cast<f32x4*>(gates_out + t * 4) = f32x4{sg[0] * inv, sg[1] * inv, sg[2] * inv, sg[3] * inv};
-        } else {
-#pragma unroll
-          for (int j = 0; j < K; ++j) gates_out[t * K + j] = sg[j] * inv;
-        }
-      }
-    }
-
-    if constexpr (EXTRA) {
-      if (logits != nullptr && t < T) {
-#pragma unroll
-        for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int ee = mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (ee < n_experts) logits[t * n_experts + ee] = acc[mb][nb][r];
-          }
-      }
-      if (lse != nullptr) {
-        float m = -__builtin_inff();
-#pragma unroll
-        for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int ee = mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (ee < n_experts) m = fmaxf(m, acc[mb][nb][r]);
-          }
-        float sum = 0.0f;
-#pragma unroll
-        for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int ee = mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (ee < n_experts) sum += __builtin_amdgcn_exp2f((acc[mb][nb][r] - m) * kLog2e);
-          }
-        const float m2 = __shfl_xor(m, 32);
-        const float sum2 = __shfl_xor(sum, 32);
-        const float mm = fmaxf(m, m2);
-        const float tot =
-            sum * __builtin_amdgcn_exp2f((m - mm) * kLog2e) + sum2 * __builtin_amdgcn_exp2f((m2 - mm) * kLog2e);
-        if (h == 0 && t < T) lse[t] = mm + __logf(tot);
-      }
-    }
-  }
-
-  } else {
-    epilogue_split<K, FULL, EXTRA, NB>(acc, tid, wave, lane, row0, T, n_experts, normalize, bv + shift, xs0, xs1, xs2,
-                                       ws0, ws1, idx_out, gates_out, logits, lse);
-  }
+  epilogue_split<K, FULL, EXTRA, NB>(acc, tid, wave, lane, row0, T, n_experts, normalize, bv + shift, xs0, xs1, xs2,
+                                     ws0, ws1, idx_out, gates_out, logits, lse);
 
   int* const hist = reinterpret_cast<int*>(ws1 + 1024);
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
@@ -415,12 +291,11 @@ hipError_t launch_kfn(const RouterArgs& a, hipStream_t stream) {
   constexpr int kTok = 4 * 32 * NB;
   const dim3 grid((unsigned)((a.T + kTok - 1) / kTok));
   int32_t* const loads = NB == kNB ? a.tile_loads : nullptr;
-  constexpr int ES = NB == kNB ? 2 : 1;  // the full tile on 8 waves, the half tile on 4
   if (a.logits != nullptr || a.lse != nullptr)
-    return launch(router_mfma_kernel<K, FULL, true, NB, ES>, grid, dim3(kThreads * ES), 0, stream,
+    return launch(router_mfma_kernel<K, FULL, true, NB>, grid, dim3(kThreads * 2), 0, stream,
                   (const uint16_t*)a.x, (const uint16_t*)a.w, a.bias, a.T, a.d, a.n_experts, normalize, a.idx,
                   a.gates, a.counts, a.logits, a.lse, loads, a.loads_stride);
-  return launch(router_mfma_kernel<K, FULL, false, NB, ES>, grid, dim3(kThreads * ES), 0, stream,
+  return launch(router_mfma_kernel<K, FULL, false, NB>, grid, dim3(kThreads * 2), 0, stream,
                 (const uint16_t*)a.x, (const uint16_t*)a.w, a.bias, a.T, a.d, a.n_experts, normalize, a.idx,
                 a.gates, a.counts, a.logits, a.lse, loads, a.loads_stride);
 }

@@ -16,6 +16,7 @@ and the CPU oracle timed on the host on the same workload.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -41,6 +42,42 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
+class TimingEvent:
+    """A HIP timing event created with hipEventDisableSystemFence, through the HIP runtime torch
+    already loaded.  Handed to a kernel launch as its stop event, it takes the kernel's own end
+    time stamp (no marker packet, no cache write-back or invalidation), as a profiler's kernel
+    trace sees it.  Duck-types the parts of torch.cuda.Event that RouterStep.set_timing and the
+    bench use."""
+
+    _hip = None
+
+    def __init__(self) -> None:
+        if TimingEvent._hip is None:
+            TimingEvent._hip = ctypes.CDLL("libamdhip64.so.7")  # resolves to the copy already loaded
+        h = ctypes.c_void_p()
+        rc = self._hip.hipEventCreateWithFlags(ctypes.byref(h), ctypes.c_uint(0x20000000))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        self.cuda_event = h.value
+
+    def record(self, stream) -> None:
+        rc = self._hip.hipEventRecord(ctypes.c_void_p(self.cuda_event), ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end: "TimingEvent") -> float:
+        ms = ctypes.c_float()
+        rc = self._hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.cuda_event),
+                                           ctypes.c_void_p(end.cuda_event))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self) -> None:
+        if TimingEvent._hip is not None and getattr(self, "cuda_event", None):
+            TimingEvent._hip.hipEventDestroy(ctypes.c_void_p(self.cuda_event))
+
+
 def router_alg_bytes(T: int, d: int, n_e: int, k: int) -> int:
     """HBM bytes the router forward must move: X once, W once, idx + gates out, b in, counts."""
     return T * (2 * d + 8 * k) + n_e * 2 * d + n_e * 4 + n_e * 4
@@ -58,12 +95,15 @@ def traffic_from_profile(T: int) -> float | None:
     return float(rec["traffic_bytes_per_launch"])
 
 
-def summarize_traffic(fetch_csv: str, write_csv: str, copy_mib: int, T: int) -> dict:
+def summarize_traffic(fetch_csv: str, write_csv: str, copy_mib: int, T: int, launches: int) -> dict:
     """HBM bytes per router launch from two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE).
 
-    Both counters report KiB per dispatch, summed here over the counter's instances.  Each is
-    scaled by what it reads for the plain device-to-device copy of known size that
-    ``--calibrate-copy`` runs in the same program (the copy reads and writes copy_mib MiB).
+    Both counters report KiB per dispatch, summed here over the counter's instances, and are
+    averaged over the last `launches` router launches: the back-to-back launches the roofline
+    times.  (Inside a step the counters of the router launch also take in the write-back of the
+    permutation the previous step's scatter left in the cache, 2 MiB more.)  Each is scaled by
+    what it reads for the plain device-to-device copy of known size that ``--calibrate-copy``
+    runs in the same program (the copy reads and writes copy_mib MiB).
     """
     import csv
     from collections import defaultdict
@@ -80,13 +120,13 @@ def summarize_traffic(fetch_csv: str, write_csv: str, copy_mib: int, T: int) -> 
     # The calibration copies are the last three blits of the program (earlier blits are the
     # host-to-device uploads of the inputs).
     copy_bytes = copy_mib * 1024 * 1024
-    f_router = per_kernel(fetch_csv, "FETCH_SIZE", "router_mfma_kernel")
-    w_router = per_kernel(write_csv, "WRITE_SIZE", "router_mfma_kernel")
+    f_router = per_kernel(fetch_csv, "FETCH_SIZE", "router_mfma_kernel", last=launches)
+    w_router = per_kernel(write_csv, "WRITE_SIZE", "router_mfma_kernel", last=launches)
     f_copy = per_kernel(fetch_csv, "FETCH_SIZE", "copyBuffer", last=3)
     w_copy = per_kernel(write_csv, "WRITE_SIZE", "copyBuffer", last=3)
     f_scale, w_scale = copy_bytes / (f_copy * 1024), copy_bytes / (w_copy * 1024)
     return {
-        "kernel_source_sha256": kernel_source_hash(), "T": T,
+        "kernel_source_sha256": kernel_source_hash(), "T": T, "launches_averaged": launches,
         "fetch_kib_per_launch": f_router, "write_kib_per_launch": w_router,
         "copy_mib": copy_mib, "copy_fetch_kib": f_copy, "copy_write_kib": w_copy,
         "fetch_scale": f_scale, "write_scale": w_scale,
@@ -122,19 +162,29 @@ def cpu_baseline(wl, x, w, b, m, min_seconds: float = 10.0, max_seconds: float =
             "seconds": round(el, 2)}
 
 
-def time_events(fn, reps: int, stream) -> float:
-    """Average ms of fn() over reps runs, HIP events on `stream` around each."""
+def time_events(fn, reps: int, stream, per_call: bool = False) -> float:
+    """Average ms of fn() over reps runs between HIP events on `stream`: back to back between two
+    events, or (per_call, for kernels of a few microseconds, whose back-to-back rate is the
+    host's launch rate) bracketed one by one with fence-free events."""
     import torch
 
     fn()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for a, b in ev:
-        a.record(stream)
+    if per_call:
+        ev = [(TimingEvent(), TimingEvent()) for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in ev) / reps
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
         fn()
-        b.record(stream)
+    b.record(stream)
     torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in ev) / reps
+    return a.elapsed_time(b) / reps
 
 
 def bench_next_rows(elb, wl, x, w, out, stream, reps: int = 20) -> dict:
@@ -146,11 +196,12 @@ def bench_next_rows(elb, wl, x, w, out, stream, reps: int = 20) -> dict:
     T, d, k, n_e = wl.T, wl.d, wl.k, wl.n_experts
     res = {}
     lse = torch.randn(T, device=x.device) + 6.0
-    res["zloss_us"] = round(time_events(lambda: elb.zloss(lse), reps, stream) * 1e3, 2)
+    res["zloss_us"] = round(time_events(lambda: elb.zloss(lse), reps, stream, per_call=True) * 1e3, 2)
     L = 60
     counts = torch.randint(0, 4 * T // n_e * 2, (L, n_e), dtype=torch.int32, device=x.device)
     bl, ml = torch.zeros((L, n_e), device=x.device), torch.zeros((L, n_e), device=x.device)
-    res["update_60_layers_us"] = round(time_events(lambda: elb.smebu_update_layers(counts, bl, ml), reps, stream) * 1e3, 2)
+    res["update_60_layers_us"] = round(time_events(lambda: elb.smebu_update_layers(counts, bl, ml), reps, stream,
+                                                         per_call=True) * 1e3, 2)
     # The permutation of this batch (from the step, or from a dispatch call when the step has none).
     inv = out.inv_perm.clone() if out.inv_perm is not None else elb.router_dispatch(out.topk_idx, n_e)[2]
     gates = out.gates.clone()
@@ -187,8 +238,8 @@ def main() -> int:
     ap.add_argument("--workload", default="large")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-next", action="store_true", help="skip the rows beside the hot path")
-    ap.add_argument("--timing-every", type=int, default=8, metavar="N",
-                    help="record the router kernel's events on every N-th timed step")
+    ap.add_argument("--router-launches", type=int, default=200, metavar="R",
+                    help="back-to-back router launches timed for the roofline")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run a device-to-device copy of MIB MiB (the byte-counter reference)")
     ap.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_MIB"),
@@ -198,7 +249,7 @@ def main() -> int:
         import datagen
 
         rec = summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1], int(args.summarize_traffic[2]),
-                                datagen.WORKLOADS[args.workload].T)
+                                datagen.WORKLOADS[args.workload].T, max(1, args.router_launches))
         with open(TRAFFIC_FILE, "w") as f:
             json.dump(rec, f, indent=1)
         print(json.dumps(rec))
@@ -240,35 +291,37 @@ def main() -> int:
                           dispatch=wl.dispatch)
     stream = torch.cuda.current_stream(dev)
 
-    # Every `timing_every`-th timed step carries events around its router kernel (recorded by the
-    # library on its stream) and one after the step; the others run bare, so the markers do not
-    # weigh on the step rate.  The router's duration is the average over the timed steps sampled.
-    every = max(1, args.timing_every)
-    timed = list(range(0, args.steps, every))
-    ev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in timed}
-    for e in ev.values():
-        for one in e:
-            one.record(stream)  # creates the HIP event before the timed region
-    torch.cuda.synchronize()
-
     for i in range(args.warmup):
         step(xs[i & 1])
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for i in range(args.steps):
-        e = ev.get(i)
-        step.set_timing(*(e[:2] if e else (None, None)))
         out = step(xs[i & 1])
-        if e:
-            e[2].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
-    router_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev.values()]))
-    rest_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev.values()]))
     value = T / (ms * 1e-3)
     mv = out.maxvio
+
+    # The router kernel's average launch duration, for the roofline: R launches of it back to
+    # back on the same stream (a step with neither dispatch nor update; the counts accumulate),
+    # from the end of an empty kernel launched just before the first to the end of the last.
+    # The events are fence-free and bound to those two kernels, so no marker sits between the
+    # launches; the one dispatch gap after the empty kernel is spread over the R launches.  (A
+    # marker beside every launch would add its own ~5 us dispatch gap to each.)  The clock of a
+    # power-limited part wanders over milliseconds, so R spans about as long as the steps do.
+    solo = elb.RouterStep(wd, bd, None, k, T, update=False, dispatch=False)
+    t0, t1 = TimingEvent(), TimingEvent()
+    n_solo = max(1, args.router_launches)
+    for i in range(2):
+        solo(xs[i & 1])
+    torch.cuda.synchronize()
+    for i in range(n_solo):
+        solo.set_timing(t0 if i == 0 else None, t1 if i == n_solo - 1 else None)
+        solo(xs[i & 1])
+    torch.cuda.synchronize()
+    router_ms = t0.elapsed_time(t1) / n_solo
 
     alg = router_alg_bytes(T, d, n_e, k)
     achieved = alg / (router_ms * 1e-3) / 1e9
@@ -293,11 +346,10 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else round(traffic),
-                     "kernel": "router_mfma_kernel<4>", "alg_bytes_per_launch": alg, "launches_timed": len(ev),
+                     "kernel": "router_mfma_kernel<4>", "alg_bytes_per_launch": alg, "launches_timed": n_solo,
                      "kernel_us": round(router_ms * 1e3, 2),
                      "mfma_tflops": round(tflops, 1), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)},
-        "breakdown_us": {"router": round(router_ms * 1e3, 2), "dispatch+update": round(rest_ms * 1e3, 2),
-                         "step": round(ms * 1e3, 2)},
+        "breakdown_us": {"step": round(ms * 1e3, 2), "router_back_to_back": round(router_ms * 1e3, 2)},
         "maxvio_last": float(mv.cpu()[0]),
     }
     if not args.no_next:

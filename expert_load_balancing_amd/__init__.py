@@ -368,16 +368,20 @@ class RouterStep:
         self._args = a
         self._timing = None
 
-    def set_timing(self, start: torch.cuda.Event | None, stop: torch.cuda.Event | None = None) -> None:
-        """Record ``start``/``stop`` (timing-enabled torch events) around the router kernel of later
-        calls; ``set_timing(None)`` stops recording."""
-        if start is None:
+    def set_timing(self, start=None, stop=None) -> None:
+        """Bracket the router kernel of later calls with timing events (torch.cuda.Event or any
+        object with a ``cuda_event`` handle): ``start`` takes the end of an empty kernel launched
+        just before it, ``stop`` the router kernel's own end; either may be None, and
+        ``set_timing()`` stops it."""
+        if start is None and stop is None:
             self._timing, self._args.timing = None, None
             return
+        handles = []
         for ev in (start, stop):
-            if ev.cuda_event == 0:  # torch creates the HIP event on first record
+            if ev is not None and ev.cuda_event == 0:  # torch creates the HIP event on first record
                 ev.record(torch.cuda.current_stream(self.device))
-        self._timing = (ctypes.c_void_p * 2)(start.cuda_event, stop.cuda_event)
+            handles.append(None if ev is None else ev.cuda_event)
+        self._timing = (ctypes.c_void_p * 2)(*handles)
         self._args.timing = ctypes.cast(self._timing, ctypes.c_void_p).value
 
     def __call__(self, x: torch.Tensor) -> StepOutputs:

@@ -125,7 +125,6 @@ elb_status elb_route_step(const elb_step_args* args, elb_stream_t stream) {
     st = check_update(a.counts, a.n_experts, a.params, a.bias, a.momentum, a.delta_b, a.maxvio);
     if (st != ELB_OK) return st;
   }
-  if (a.timing != nullptr && (a.timing[0] == nullptr || a.timing[1] == nullptr)) return ELB_ERR_NULL;
   if (a.zloss != nullptr && a.lse == nullptr) return ELB_ERR_NULL;
   if (!aligned(a.zloss, 4)) return ELB_ERR_ALIGN;
 
@@ -140,14 +139,18 @@ elb_status elb_route_step(const elb_step_args* args, elb_stream_t stream) {
   const bool mfma = !(a.flags & ELB_FORCE_GENERIC) && elb::router_mfma_applies(ra);
   const bool loads_ready = dispatch && mfma && elb::router_mfma_full_tile(a.T);  // the router fills the table
   if (!loads_ready) ra.tile_loads = nullptr;
-  if (a.timing != nullptr && hipEventRecord(static_cast<hipEvent_t>(a.timing[0]), s) != hipSuccess)
-    return ELB_ERR_LAUNCH;
+  if (a.timing != nullptr) {
+    // From the end of an empty kernel launched just before the router kernel to its end.
+    if (a.timing[0] != nullptr && elb::launch_mark(static_cast<hipEvent_t>(a.timing[0]), s) != hipSuccess)
+      return ELB_ERR_LAUNCH;
+    ra.ev_stop = static_cast<hipEvent_t>(a.timing[1]);
+  }
   if (a.T > 0) {
     const hipError_t err = mfma ? elb::launch_router_mfma(ra, s) : elb::launch_router_generic(ra, s);
     if (err != hipSuccess) return ELB_ERR_LAUNCH;
-  }
-  if (a.timing != nullptr && hipEventRecord(static_cast<hipEvent_t>(a.timing[1]), s) != hipSuccess)
+  } else if (ra.ev_stop != nullptr && elb::launch_mark(ra.ev_stop, s) != hipSuccess) {  // no router kernel
     return ELB_ERR_LAUNCH;
+  }
   if (a.zloss != nullptr && elb::launch_zloss(a.lse, a.T, a.zloss, s) != hipSuccess) return ELB_ERR_LAUNCH;
   const elb::BalanceArgs upd =
       balance_args(a.counts, a.n_experts, a.params, a.bias, a.momentum, a.delta_b, a.maxvio);

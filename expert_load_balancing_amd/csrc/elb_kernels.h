@@ -2,6 +2,7 @@
 // Not installed; the public interface is include/elb.h.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -28,6 +29,7 @@ struct RouterArgs {
   float* lse;
   int32_t* tile_loads;   // NULL, or the dispatch workspace's [n_experts][loads_stride] table:
   int64_t loads_stride;  // the MFMA kernel then stores each 256-token tile's loads in it
+  hipEvent_t ev_stop = nullptr;  // NULL, or an event that takes the router kernel's end time stamp
 };
 
 // One bias update / MaxVio (balance_wave.hpp).  mode < 0: MaxVio only.
@@ -43,20 +45,32 @@ struct BalanceArgs {
   float* maxvio;
 };
 
-// Launch `kernel` and return the runtime's launch status instead of dropping it.
+// Launch `kernel` and return the runtime's launch status instead of dropping it.  With an event
+// created with hipEventDisableSystemFence as ev_stop, the dispatch itself stamps its end time
+// into it (hipExtLaunchKernel); ev_start is recorded as a marker just before the dispatch.
 template <typename... KArgs, typename... Args>
-hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem, hipStream_t stream,
-                  Args&&... args) {
+hipError_t launch_timed(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem, hipStream_t stream,
+                        hipEvent_t ev_start, hipEvent_t ev_stop, Args&&... args) {
   std::tuple<KArgs...> held(std::forward<Args>(args)...);
   void* ptrs[sizeof...(KArgs)];
   std::apply([&](auto&... a) {
     int i = 0;
     ((ptrs[i++] = static_cast<void*>(&a)), ...);
   }, held);
-  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, shmem, stream);
+  if (ev_start == nullptr && ev_stop == nullptr)
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, shmem, stream);
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, shmem, stream, ev_start,
+                            ev_stop, 0);
+}
+template <typename... KArgs, typename... Args>
+hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem, hipStream_t stream,
+                  Args&&... args) {
+  return launch_timed(kernel, grid, block, shmem, stream, nullptr, nullptr, std::forward<Args>(args)...);
 }
 
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t value, hipStream_t stream);
+// An empty one-wave kernel whose end time stamp goes into `ev`.
+hipError_t launch_mark(hipEvent_t ev, hipStream_t stream);
 
 bool router_mfma_applies(const RouterArgs& a);
 // true: the MFMA router runs 256-token tiles for T tokens and fills the dispatch's loads table;

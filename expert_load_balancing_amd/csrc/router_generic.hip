@@ -159,12 +159,12 @@ hipError_t launch_router_generic(const RouterArgs& a, hipStream_t stream) {
   const int grid = (int)(n_groups < 2048 ? n_groups : 2048);
   const int normalize = (a.flags & ELB_GATES_RAW) ? 0 : 1;
   if (a.dtype == ELB_F32)
-    return launch(router_generic_kernel<float>, dim3(grid), dim3(kThreads), 0, stream, (const float*)a.x,
-                  (const float*)a.w, a.bias, a.T, a.d, a.n_experts, a.k, normalize, a.idx, a.gates, a.counts,
-                  a.logits, a.lse);
-  return launch(router_generic_kernel<uint16_t>, dim3(grid), dim3(kThreads), 0, stream, (const uint16_t*)a.x,
-                (const uint16_t*)a.w, a.bias, a.T, a.d, a.n_experts, a.k, normalize, a.idx, a.gates, a.counts,
-                a.logits, a.lse);
+    return launch_timed(router_generic_kernel<float>, dim3(grid), dim3(kThreads), 0, stream, nullptr, a.ev_stop,
+                        (const float*)a.x, (const float*)a.w, a.bias, a.T, a.d, a.n_experts, a.k, normalize, a.idx,
+                        a.gates, a.counts, a.logits, a.lse);
+  return launch_timed(router_generic_kernel<uint16_t>, dim3(grid), dim3(kThreads), 0, stream, nullptr, a.ev_stop,
+                      (const uint16_t*)a.x, (const uint16_t*)a.w, a.bias, a.T, a.d, a.n_experts, a.k, normalize,
+                      a.idx, a.gates, a.counts, a.logits, a.lse);
 }
 
 }  // namespace elb

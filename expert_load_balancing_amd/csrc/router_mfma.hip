@@ -292,12 +292,12 @@ hipError_t launch_kfn(const RouterArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)((a.T + kTok - 1) / kTok));
   int32_t* const loads = NB == kNB ? a.tile_loads : nullptr;
   if (a.logits != nullptr || a.lse != nullptr)
-    return launch(router_mfma_kernel<K, FULL, true, NB>, grid, dim3(kThreads * 2), 0, stream,
-                  (const uint16_t*)a.x, (const uint16_t*)a.w, a.bias, a.T, a.d, a.n_experts, normalize, a.idx,
-                  a.gates, a.counts, a.logits, a.lse, loads, a.loads_stride);
-  return launch(router_mfma_kernel<K, FULL, false, NB>, grid, dim3(kThreads * 2), 0, stream,
-                (const uint16_t*)a.x, (const uint16_t*)a.w, a.bias, a.T, a.d, a.n_experts, normalize, a.idx,
-                a.gates, a.counts, a.logits, a.lse, loads, a.loads_stride);
+    return launch_timed(router_mfma_kernel<K, FULL, true, NB>, grid, dim3(kThreads * 2), 0, stream, nullptr, a.ev_stop,
+                        (const uint16_t*)a.x, (const uint16_t*)a.w, a.bias, a.T, a.d, a.n_experts, normalize, a.idx,
+                        a.gates, a.counts, a.logits, a.lse, loads, a.loads_stride);
+  return launch_timed(router_mfma_kernel<K, FULL, false, NB>, grid, dim3(kThreads * 2), 0, stream, nullptr, a.ev_stop,
+                      (const uint16_t*)a.x, (const uint16_t*)a.w, a.bias, a.T, a.d, a.n_experts, normalize, a.idx,
+                      a.gates, a.counts, a.logits, a.lse, loads, a.loads_stride);
 }
 
 template <int K, bool FULL>

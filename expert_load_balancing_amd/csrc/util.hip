@@ -11,7 +11,15 @@ __global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* __restrict__ p, 
     p[i] = value;
 }
 
+// Does nothing: a time stamp in the stream.  The next kernel starts as it ends, with no barrier
+// packet between them (an event record puts one there and delays the next dispatch).
+__global__ __launch_bounds__(64) void mark_kernel() {}
+
 }  // namespace
+
+hipError_t launch_mark(hipEvent_t ev, hipStream_t stream) {
+  return launch_timed(mark_kernel, dim3(1), dim3(64), 0, stream, nullptr, ev);
+}
 
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t value, hipStream_t stream) {
   if (n <= 0) return hipSuccess;

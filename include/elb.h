@@ -170,8 +170,13 @@ elb_status elb_smebu_update(int32_t* counts, int32_t n_experts, elb_balance_para
  * if any, runs as its own launch after the router kernel.
  * The MFMA router takes 128-token tiles for batches of at most 128 x 256 tokens (so that every
  * compute unit gets a tile); the dispatch then counts the loads itself.
- * timing: NULL, or two hipEvent_t recorded on `stream` right before and right after the
- * router kernel (a measuring aid; both must be valid events).
+ * timing: NULL, or two hipEvent_t (either may be NULL) that bracket the router kernel: the
+ * first takes the end time stamp of an empty one-wave kernel launched right before it, the
+ * second the router kernel's own end (both through hipExtLaunchKernel; with T == 0 the empty
+ * kernel stands in for the router kernel).  Events created with hipEventDisableSystemFence are
+ * bound to the kernels' time stamps; with other events the runtime records markers after the
+ * kernels, which adds their cost to the interval.  Either way the next kernel starts a few
+ * microseconds later than it would without the event.  A measuring aid.
  */
 typedef struct {
   /* elb_router_forward */

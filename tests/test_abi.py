@@ -164,12 +164,6 @@ def test_route_step_null_args(lib):
     assert lib.elb_route_step(None, None) == NULL
 
 
-def test_route_step_half_timing_pair(lib):
-    pair = (ctypes.c_void_p * 2)(FAKE, None)
-    a = step_args(timing=ctypes.cast(pair, ctypes.c_void_p).value)
-    assert lib.elb_route_step(ctypes.byref(a), None) == NULL
-
-
 def _c_layout(struct: str, fields: list[str], tmp_path) -> dict:
     """offsetof/sizeof of a struct of include/elb.h as the host C compiler lays it out."""
     src = tmp_path / "layout.c"

@@ -122,20 +122,40 @@ def test_step_empty_batch_still_updates():
     assert (bd.cpu().numpy() == b1).all() and np.isnan(out.maxvio.cpu().numpy()).all()
 
 
-def test_step_timing_events():
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])  # the MFMA kernel and the generic one
+def test_step_timing_events(dtype):
+    """Events handed to the step bracket the router kernel; the routing is the same with and
+    without them, and an empty batch gives a (near) empty interval."""
     T, d, n_e, k = 1024, 512, 256, 4
-    _, x, w, b0 = make(T, d, n_e, k, seed=2)
-    step = elb.RouterStep(to_dev(w), to_dev(b0), torch.zeros(n_e, device="cuda"), k, T)
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    step.set_timing(start, stop)
+    _, x, w, b0 = make(T, d, n_e, k, dtype=dtype, seed=2)
     xd = to_dev(x)
-    step(xd)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(stop)
-    assert 0.0 < ms < 100.0, ms
-    step.set_timing(None)
-    step(xd)
-    torch.cuda.synchronize()
+    outs = []
+    for timed in (True, False):
+        step = elb.RouterStep(to_dev(w), to_dev(b0), torch.zeros(n_e, device="cuda"), k, T, update=False)
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if timed:
+            step.set_timing(start, stop)
+        out = step(xd)
+        torch.cuda.synchronize()
+        if timed:
+            ms = start.elapsed_time(stop)
+            assert 0.0 < ms < 100.0, ms
+            step(xd[:0])
+            torch.cuda.synchronize()
+            assert 0.0 <= start.elapsed_time(stop) < 100.0
+            # One event per call: from before the first router kernel to the end of the second.
+            step.set_timing(start, None)
+            step(xd)
+            step.set_timing(None, stop)
+            step(xd)
+            torch.cuda.synchronize()
+            assert 0.0 < start.elapsed_time(stop) < 200.0
+            step.set_timing()
+            out = step(xd)
+            torch.cuda.synchronize()
+        outs.append([t.cpu().numpy() for t in (out.topk_idx, out.gates)])
+    for a, b in zip(*outs):
+        assert (a == b).all()
 
 
 def test_route_step_without_dispatch_matches():

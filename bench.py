@@ -78,6 +78,11 @@ class TimingEvent:
             TimingEvent._hip.hipEventDestroy(ctypes.c_void_p(self.cuda_event))
 
 
+def dispatch_alg_bytes(T: int, n_e: int, k: int) -> int:
+    """HBM bytes the dispatch must move: idx in once, perm and inv out, offsets out."""
+    return T * k * 4 * 3 + (n_e + 1) * 4
+
+
 def router_alg_bytes(T: int, d: int, n_e: int, k: int) -> int:
     """HBM bytes the router forward must move: X once, W once, idx + gates out, b in, counts."""
     return T * (2 * d + 8 * k) + n_e * 2 * d + n_e * 4 + n_e * 4
@@ -323,6 +328,21 @@ def main() -> int:
     torch.cuda.synchronize()
     router_ms = t0.elapsed_time(t1) / n_solo
 
+    # The dispatch (a6) through its own entry point, on the last step's indices, back to back:
+    # the counting pass, the scan and the scatter (inside the step the router kernel has done the
+    # counting).  It moves ~1% of the router's bytes and is bound by latency, not bandwidth.
+    dispatch = None
+    if wl.dispatch:
+        ws_d = torch.empty(elb.dispatch_workspace_bytes(T, k, n_e), dtype=torch.uint8, device=dev)
+        idx_last = out.topk_idx.clone()
+        outs = (torch.empty(n_e + 1, dtype=torch.int32, device=dev), torch.empty(T * k, dtype=torch.int32, device=dev),
+                torch.empty(T * k, dtype=torch.int32, device=dev))
+        ms_d = time_events(lambda: elb.router_dispatch(idx_last, n_e, workspace=ws_d, out=outs), 50, stream)
+        alg_d = dispatch_alg_bytes(T, n_e, k)
+        dispatch = {"us": round(ms_d * 1e3, 2), "kernels": 3, "alg_bytes": alg_d,
+                    "achieved_GBps": round(alg_d / (ms_d * 1e-3) / 1e9, 1),
+                    "frac": round(alg_d / (ms_d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
     alg = router_alg_bytes(T, d, n_e, k)
     achieved = alg / (router_ms * 1e-3) / 1e9
     flops = 2.0 * T * d * n_e
@@ -350,6 +370,7 @@ def main() -> int:
                      "kernel_us": round(router_ms * 1e3, 2),
                      "mfma_tflops": round(tflops, 1), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)},
         "breakdown_us": {"step": round(ms * 1e3, 2), "router_back_to_back": round(router_ms * 1e3, 2)},
+        "dispatch": dispatch,
         "maxvio_last": float(mv.cpu()[0]),
     }
     if not args.no_next:

@@ -127,8 +127,11 @@ def dispatch_workspace_bytes(T: int, k: int, n_experts: int) -> int:
 
 
 def router_dispatch(topk_idx: torch.Tensor, n_experts: int, *, workspace: torch.Tensor | None = None,
-                    want_inv: bool = True):
-    """Stable counting sort of topk_idx [T, k] by expert: (offsets [N_r+1], perm [T*k], inv [T*k] or None)."""
+                    want_inv: bool = True, out: tuple | None = None):
+    """Stable counting sort of topk_idx [T, k] by expert: (offsets [N_r+1], perm [T*k], inv [T*k] or None).
+
+    ``out``: (offsets, perm, inv or None) int32 tensors to write instead of new ones.
+    """
     _need(topk_idx, "topk_idx", torch.int32)
     dev = topk_idx.device
     T, k = topk_idx.shape
@@ -137,9 +140,18 @@ def router_dispatch(topk_idx: torch.Tensor, n_experts: int, *, workspace: torch.
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     else:
         _need(workspace, "workspace", device=dev)
-    offsets = torch.empty(n_experts + 1, dtype=torch.int32, device=dev)
-    perm = torch.empty(T * k, dtype=torch.int32, device=dev)
-    inv = torch.empty(T * k, dtype=torch.int32, device=dev) if want_inv else None
+    if out is not None:
+        offsets, perm, inv = out
+        _need(offsets, "offsets", torch.int32, dev)
+        _need(perm, "perm", torch.int32, dev)
+        if inv is not None:
+            _need(inv, "inv", torch.int32, dev)
+        if offsets.numel() != n_experts + 1 or perm.numel() != T * k or (inv is not None and inv.numel() != T * k):
+            raise ValueError("router_dispatch: out tensors have the wrong sizes")
+    else:
+        offsets = torch.empty(n_experts + 1, dtype=torch.int32, device=dev)
+        perm = torch.empty(T * k, dtype=torch.int32, device=dev)
+        inv = torch.empty(T * k, dtype=torch.int32, device=dev) if want_inv else None
     nbytes = workspace.numel() * workspace.element_size()
     st = lib().elb_router_dispatch(_ptr(topk_idx), T, k, n_experts, _ptr(workspace), nbytes, _ptr(offsets),
                                    _ptr(perm), _ptr(inv), _stream(dev))

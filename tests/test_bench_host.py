@@ -29,6 +29,12 @@ def test_router_alg_bytes_large_workload():
     assert bench.router_alg_bytes(T, d, n_e, k) == 406_325_248
 
 
+def test_dispatch_alg_bytes_large_workload():
+    # idx in (16 B per token at K = 4), perm and inv out (32 B per token), offsets out.
+    T, n_e, k = 65536, 256, 4
+    assert bench.dispatch_alg_bytes(T, n_e, k) == T * 16 + T * 32 + (n_e + 1) * 4
+
+
 def _counter_csv(path, counter, rows):
     """rows: (dispatch id, kernel name, [values of the counter's instances])."""
     fields = ["Correlation_Id", "Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]

@@ -66,6 +66,26 @@ def test_dispatch_without_inverse_and_reused_workspace():
         check_dispatch(offs.cpu().numpy(), perm.cpu().numpy(), None, idx, 256)
 
 
+def test_dispatch_into_given_outputs():
+    """out=: the same permutation written into the caller's tensors (stale contents first);
+    outputs of the wrong size are refused before any launch."""
+    rng = np.random.default_rng(5)
+    idx = rng.integers(0, 200, size=(4500, 3)).astype(np.int32)
+    outs = (torch.full((201,), -7, dtype=torch.int32, device="cuda"),
+            torch.full((13500,), -7, dtype=torch.int32, device="cuda"),
+            torch.full((13500,), -7, dtype=torch.int32, device="cuda"))
+    offs, perm, inv = elb.router_dispatch(to_dev(idx), 200, out=outs)
+    torch.cuda.synchronize()
+    assert offs is outs[0] and perm is outs[1] and inv is outs[2]
+    check_dispatch(offs.cpu().numpy(), perm.cpu().numpy(), inv.cpu().numpy(), idx, 200)
+    ref = elb.router_dispatch(to_dev(idx), 200)
+    torch.cuda.synchronize()
+    for a, b in zip((offs, perm, inv), ref):
+        assert torch.equal(a, b)
+    with pytest.raises(ValueError):
+        elb.router_dispatch(to_dev(idx), 200, out=(outs[0], outs[1][:100], None))
+
+
 WL = datagen.WORKLOADS["large"]
 
 

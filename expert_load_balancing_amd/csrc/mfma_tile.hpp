@@ -208,16 +208,21 @@ struct KRows {
 // 256 / ES of the A rows (ES = 2: 8 waves, two per SIMD, so that one wave's stalled DMA or LDS
 // read leaves the other issuing MFMAs).  Wave w owns A blocks (w % ES) * kMB / ES .. and B blocks
 // (w / ES) * NB ...  A's rows are `a_row_bytes` apart, B's `b_row_bytes`; `nkb` stages of kBK
-// elements are contracted (nkb >= 1).
-template <int AUX_A, int AUX_B, class LA = RowsK, class LB = RowsK, int NB = kNB, int ES = 1>
+// elements are contracted (nkb >= 1).  PR (with ES = 2): only waves kWaves .. 2 kWaves - 1 (one
+// per SIMD) issue the DMAs, twice their share each; the other wave of each SIMD only reads LDS
+// and issues MFMAs, so no DMA that waits for room in the vector memory pipeline ever holds up
+// its MFMAs (a wave issues in order).
+template <int AUX_A, int AUX_B, class LA = RowsK, class LB = RowsK, int NB = kNB, int ES = 1, bool PR = false>
 struct Stream {
   static_assert(NB == kNB || (NB == 1 && LB::kReads == 1), "a 128-row B tile is laid out rows-contiguous-in-k");
   static_assert(ES == 1 || (ES == 2 && LA::kReads == 1 && LB::kReads == 1), "the 8-wave split: rows-contiguous-in-k");
+  static_assert(!PR || ES == 2, "DMA-issuing waves need a second wave per SIMD");
   static constexpr int kWavesS = kWaves * ES;
   static constexpr int kMBw = kMB / ES;  // A blocks per wave
-  // DMA instructions per wave per stage (1 KiB each): A's 256 rows, B's 128 NB rows, over the waves.
-  static constexpr int kDmaA = kDma / ES;
-  static constexpr int kDmaB = kDma * NB / kNB / ES;
+  // DMA instructions per issuing wave per stage (1 KiB each): A's 256 rows, B's 128 NB rows,
+  // over the waves that issue them.
+  static constexpr int kDmaA = PR ? kDma : kDma / ES;
+  static constexpr int kDmaB = PR ? kDma * NB / kNB : kDma * NB / kNB / ES;
   // VMEM instructions a wave issues after the DMAs of stage j's A rows, when it must have stage
   // j: the B DMAs of the same iteration, then (kPW - 1) full iterations.
   static constexpr int kBudget = kDmaB + (kDmaA + kDmaB) * (kPW - 1);
@@ -225,6 +230,7 @@ struct Stream {
   uint32_t voa[kDmaA], vob[kDmaB];
   uint32_t wave_off_a, wave_off_b, a_stage, b_stage;
   int nkb;
+  bool issues;  // this wave issues DMAs
   Slots sl;
 
   // a_bytes / b_bytes: the readable bytes of each operand from its base (rows past them read 0).
@@ -236,12 +242,15 @@ struct Stream {
     none = make_rsrc(a, 0u);
     nkb = n_stages;
     sl = slots;
+    issues = !PR || wave >= kWaves;
+    const int dw = PR ? (wave >= kWaves ? wave - kWaves : 0) : wave;  // the wave's share of the DMAs
+    constexpr int kSharers = PR ? kWaves : kWavesS;
 #pragma unroll
-    for (int i = 0; i < kDmaA; ++i) voa[i] = LA::dma_off(wave, lane, i, a_row_bytes, 64 / ES);
+    for (int i = 0; i < kDmaA; ++i) voa[i] = LA::dma_off(dw, lane, i, a_row_bytes, 256 / kSharers);
 #pragma unroll
-    for (int i = 0; i < kDmaB; ++i) vob[i] = LB::dma_off(wave, lane, i, b_row_bytes, 32 * NB / ES);
-    wave_off_a = (uint32_t)wave * (kDmaA * 1024);  // A: 64 rows x 128 B or 16 rows x 512 B
-    wave_off_b = (uint32_t)wave * (kDmaB * 1024);
+    for (int i = 0; i < kDmaB; ++i) vob[i] = LB::dma_off(dw, lane, i, b_row_bytes, 128 * NB / kSharers);
+    wave_off_a = (uint32_t)dw * (kDmaA * 1024);  // A: 64 rows x 128 B or 16 rows x 512 B
+    wave_off_b = (uint32_t)dw * (kDmaB * 1024);
     a_stage = LA::stage_bytes(a_row_bytes);
     b_stage = LB::stage_bytes(b_row_bytes);
   }
@@ -249,6 +258,7 @@ struct Stream {
   // Stages 0..kPX-1 of B and 0..kPW-1 of A, issued in the same order the steady state uses
   // (A first, then B, per virtual iteration).
   __device__ __forceinline__ void prologue() {
+    if (!issues) return;
 #pragma unroll
     for (int vi = -kPX; vi < 0; ++vi) {
       if (vi + kPW >= 0)
@@ -262,6 +272,18 @@ struct Stream {
   // acc <- the product over all nkb stages (after prologue()).  On return every DMA has landed
   // and every wave is past its last operand read (the slots may be reused).
   __device__ __forceinline__ void run(f32x16 (&acc)[kMBw][NB], int wave, int lane) {
+    if constexpr (PR) {
+      if (issues)
+        run_as<true>(acc, wave, lane);
+      else
+        run_as<false>(acc, wave, lane);
+    } else {
+      run_as<true>(acc, wave, lane);
+    }
+  }
+
+  template <bool DMA>
+  __device__ __forceinline__ void run_as(f32x16 (&acc)[kMBw][NB], int wave, int lane) {
     typename LA::Lane la;
     typename LB::Lane lb;
     la.init(lane);
@@ -286,16 +308,18 @@ struct Stream {
         if (j >= nkb) break;
         // Own DMAs of stage j are done; after the barrier everyone's are, and every wave has
         // finished reading stage j - 1, whose slots the DMAs below overwrite.
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kBudget) & ~(15 << 8));  // and lgkmcnt(0)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(DMA ? kBudget : 63) & ~(15 << 8));  // and lgkmcnt(0)
         bare_barrier();
         // A DMAs at the head of the stage (they must precede this stage's B DMAs for the vmcnt
         // budget); the B DMAs are spread over the MFMA stream below, so that a DMA waiting for
         // room in the vector memory pipeline only delays MFMAs already queued.
-        dma_rows<AUX_A, kDmaA>(ar, none, sl.w((u + kPW) % kNW) + wave_off_a, voa, (uint32_t)(j + kPW) * a_stage,
-                        j + kPW < nkb);
-        __builtin_amdgcn_sched_barrier(0);
-        dma_rows<AUX_B, kDmaB>(br, none, sl.x((u + kPX) % kNX) + wave_off_b, vob, (uint32_t)(j + kPX) * b_stage,
-                        j + kPX < nkb);
+        if constexpr (DMA) {
+          dma_rows<AUX_A, kDmaA>(ar, none, sl.w((u + kPW) % kNW) + wave_off_a, voa, (uint32_t)(j + kPW) * a_stage,
+                                 j + kPW < nkb);
+          __builtin_amdgcn_sched_barrier(0);
+          dma_rows<AUX_B, kDmaB>(br, none, sl.x((u + kPX) % kNX) + wave_off_b, vob, (uint32_t)(j + kPX) * b_stage,
+                                 j + kPX < nkb);
+        }
         const unsigned char* ws = sl.w(u % kNW);
         const unsigned char* xs = sl.x(u % kNX);
         // Operand fragments are double-buffered: the LDS reads of k-step s + 1 go out before
@@ -330,7 +354,9 @@ struct Stream {
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * kReadsStep, 0);  // DS reads, steps 0 and 1
 #pragma unroll
         for (int s = 0; s < kKSteps; ++s) {
-          if constexpr (kMfmaPerDma <= kMBw * NB) {
+          if constexpr (!DMA) {
+            __builtin_amdgcn_sched_group_barrier(0x008, kMBw * NB, 0);  // MFMAs, step s
+          } else if constexpr (kMfmaPerDma <= kMBw * NB) {
 #pragma unroll
             for (int q = 0; q < kMBw * NB / kMfmaPerDma; ++q) {
               __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerDma, 0);  // MFMAs, step s

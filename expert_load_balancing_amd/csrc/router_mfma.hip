@@ -256,7 +256,7 @@ __global__ __launch_bounds__(kThreads * 2) __attribute__((amdgpu_waves_per_eu(2,
 
   // ---- operand streams: start the DMA ring (A = weights, B = this tile's tokens) ----
   const uint32_t row_bytes = (uint32_t)d * 2u;
-  Stream<kAuxCached, kAuxStream, RowsK, RowsK, NB, 2> st;
+  Stream<kAuxCached, kAuxStream, RowsK, RowsK, NB, 2, true> st;
   st.init(w, (uint32_t)n_experts * row_bytes, row_bytes, x + row0 * d, (uint32_t)rows * row_bytes, row_bytes,
           d / kBK, wave, lane, Slots{xs0, xs1, xs2, ws0, ws1});
   st.prologue();

@@ -31,7 +31,17 @@ __global__ __launch_bounds__(kZThreads) void zloss_kernel(const float* __restric
                                                           float* __restrict__ out) {
   __shared__ double part[kZThreads / 64];
   double acc = 0.0;
-  for (int64_t i = threadIdx.x; i < T; i += kZThreads) {
+  // Eight loads in flight per thread, then the adds in index order (the same order, and so the
+  // same bits, as one element at a time).
+  int64_t i = threadIdx.x;
+  for (; i + 7 * kZThreads < T; i += 8 * kZThreads) {
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = lse[i + q * kZThreads];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc += (double)v[q] * (double)v[q];
+  }
+  for (; i < T; i += kZThreads) {
     const double v = lse[i];
     acc += v * v;
   }

@@ -47,7 +47,7 @@ def combine_bound(eo64, g, inv, k):
 
 # ------------------------------------------------------------------------- z-loss (F1)
 
-@pytest.mark.parametrize("T", [0, 1, 1000, 1025, 70001])
+@pytest.mark.parametrize("T", [0, 1, 1000, 1025, 8191, 8192, 16385, 70001])
 def test_zloss_matches_oracle(T):
     rng = np.random.default_rng(T + 5)
     lse = (rng.standard_normal(T) * 3 + 5).astype(np.float32)

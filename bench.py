@@ -289,8 +289,8 @@ def main() -> int:
     xs = [to_dev(x), to_dev(x)]
     wd, bd, md = to_dev(w), to_dev(b0), to_dev(m0)
     T, d, n_e, k = wl.T, wl.d, wl.n_experts, wl.k
-    # One library call per step (elb_route_step): router kernel, dispatch scan with the bias
-    # update beside it, scatter (workloads without dispatch: router kernel, then the update).
+    # One library call per step (elb_route_step): router kernel, dispatch scan, scatter with the
+    # bias update beside it (workloads without dispatch: router kernel, then the update).
     # The loads accumulate into counts and the update clears them.
     step = elb.RouterStep(wd, bd, md, k, T, mode=wl.mode, lam=wl.lam, beta=wl.beta, kappa=wl.kappa, gamma=wl.gamma,
                           dispatch=wl.dispatch)

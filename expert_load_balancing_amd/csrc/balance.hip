@@ -1,6 +1,6 @@
 // Expert-bias update / MaxVio launches (the arithmetic and its citations live in
-// balance_wave.hpp, which the dispatch scan also runs as an extra workgroup when a routed step
-// asks for the update), and the router z-loss reduction.
+// balance_wave.hpp, which the dispatch scatter also runs as an extra workgroup when a routed
+// step asks for the update), and the router z-loss reduction.
 #include "balance_wave.hpp"
 
 namespace elb {

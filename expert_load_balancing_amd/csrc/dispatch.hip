@@ -13,10 +13,11 @@
 //   totals [n_experts] int32.
 //  1. loads:   one workgroup per tile, LDS histogram.  Skipped when the MFMA router kernel
 //              already stored its own tile histogram in the table.
-//  2. scan:    one wave per expert scans its row in place and writes the expert's total.  With
-//              a bias update requested, one more workgroup runs it (balance_wave.hpp): the
-//              update reads only `counts`, which are final once the router kernel is done.
-//  3. scatter: one workgroup per tile, one pass.  Each block scans the expert totals itself
+//  2. scan:    one wave per expert scans its row in place and writes the expert's total.
+//  3. scatter: one workgroup per tile, one pass.  With a bias update requested, one more
+//              workgroup runs it (balance_wave.hpp): the update reads only `counts`, which are
+//              final once the router kernel is done, and its few microseconds of dependent
+//              memory round trips hide behind the scatter's (the scan is shorter).  Each block scans the expert totals itself
 //              (a few hundred cycles) for the bucket starts.  Entry c * 256 + tid of the tile
 //              goes to thread tid; each 64-entry run ("virtual wave" v = c * 4 + wave, in
 //              ascending j) ranks its lanes by expert with 8 ballots (one per bit of e), the
@@ -61,15 +62,10 @@ __global__ __launch_bounds__(kThreads) void dispatch_loads_kernel(const int32_t*
   if ((int)threadIdx.x < n_experts) loads[(int64_t)threadIdx.x * stride + blockIdx.x] = hist[threadIdx.x];
 }
 
-// Blocks 0 .. n_experts-1: scan one row each.  Block n_experts (launched only with an update):
-// the bias update.
+// Block e < n_experts scans row e.
 __global__ __launch_bounds__(64) void dispatch_scan_kernel(int32_t* __restrict__ loads, int64_t n_tiles,
                                                            int64_t stride, int n_experts,
-                                                           int32_t* __restrict__ totals, BalanceArgs update) {
-  if ((int)blockIdx.x == n_experts) {
-    balance_wave(update);
-    return;
-  }
+                                                           int32_t* __restrict__ totals) {
   const int lane = threadIdx.x;
   int32_t* const row = loads + (int64_t)blockIdx.x * stride;
   int carry = 0;
@@ -97,7 +93,12 @@ __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(const int32_
                                                                     const int32_t* __restrict__ totals,
                                                                     int32_t* __restrict__ offsets,
                                                                     int32_t* __restrict__ perm,
-                                                                    int32_t* __restrict__ inv) {
+                                                                    int32_t* __restrict__ inv, BalanceArgs update) {
+  if ((int64_t)blockIdx.x == (total + kDispatchTile * K - 1) / (kDispatchTile * K)) {
+    // The block after the last tile (launched only with an update): the bias update, one wave.
+    if (threadIdx.x < 64) balance_wave(update);
+    return;
+  }
   __shared__ int wsum[kWaves];
   __shared__ int vcnt[K * kWaves][kMaxExperts];  // per virtual wave: count, then start
   const int tid = threadIdx.x;
@@ -171,9 +172,11 @@ __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(const int32_
 template <int K>
 hipError_t launch_scatter(const int32_t* idx, int64_t total, int n_experts, const DispatchGeom& g,
                           const int32_t* loads, const int32_t* totals, int32_t* offsets, int32_t* perm, int32_t* inv,
-                          hipStream_t stream) {
-  return launch(dispatch_scatter_kernel<K>, dim3((unsigned)g.n_tiles), dim3(kThreads), 0, stream, idx, total,
-                n_experts, g.stride, loads, totals, offsets, perm, inv);
+                          const BalanceArgs* update, hipStream_t stream) {
+  const BalanceArgs none{};
+  return launch(dispatch_scatter_kernel<K>, dim3((unsigned)(g.n_tiles + (update != nullptr ? 1 : 0))), dim3(kThreads),
+                0, stream, idx, total, n_experts, g.stride, loads, totals, offsets, perm, inv,
+                update != nullptr ? *update : none);
 }
 
 }  // namespace
@@ -209,21 +212,20 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t T, int k, int n_experts, 
                  n_experts, g.stride, loads);
     if (err != hipSuccess) return err;
   }
-  const BalanceArgs none{};
-  err = launch(dispatch_scan_kernel, dim3((unsigned)(n_experts + (update != nullptr ? 1 : 0))), dim3(64), 0, stream,
-               loads, g.n_tiles, g.stride, n_experts, totals, update != nullptr ? *update : none);
+  err = launch(dispatch_scan_kernel, dim3((unsigned)n_experts), dim3(64), 0, stream, loads, g.n_tiles, g.stride,
+               n_experts, totals);
   if (err != hipSuccess) return err;
   const int32_t* cl = loads;
   const int32_t* ct = totals;
   switch (k) {
-    case 1: return launch_scatter<1>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, stream);
-    case 2: return launch_scatter<2>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, stream);
-    case 3: return launch_scatter<3>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, stream);
-    case 4: return launch_scatter<4>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, stream);
-    case 5: return launch_scatter<5>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, stream);
-    case 6: return launch_scatter<6>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, stream);
-    case 7: return launch_scatter<7>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, stream);
-    default: return launch_scatter<8>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, stream);
+    case 1: return launch_scatter<1>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, update, stream);
+    case 2: return launch_scatter<2>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, update, stream);
+    case 3: return launch_scatter<3>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, update, stream);
+    case 4: return launch_scatter<4>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, update, stream);
+    case 5: return launch_scatter<5>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, update, stream);
+    case 6: return launch_scatter<6>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, update, stream);
+    case 7: return launch_scatter<7>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, update, stream);
+    default: return launch_scatter<8>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, update, stream);
   }
 }
 

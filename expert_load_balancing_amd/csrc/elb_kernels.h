@@ -89,7 +89,7 @@ struct DispatchGeom {
 DispatchGeom dispatch_geometry(int64_t T);
 size_t dispatch_workspace_bytes(int64_t T, int n_experts);
 // loads_ready: the router kernel already filled the loads table for this batch.
-// update: NULL, or a bias update to run beside the scan (one extra workgroup).
+// update: NULL, or a bias update to run beside the scatter (one extra workgroup).
 hipError_t launch_dispatch(const int32_t* idx, int64_t T, int k, int n_experts, void* workspace, bool loads_ready,
                            const BalanceArgs* update, int32_t* offsets, int32_t* perm, int32_t* inv,
                            hipStream_t stream);

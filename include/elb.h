@@ -162,7 +162,7 @@ elb_status elb_smebu_update(int32_t* counts, int32_t n_experts, elb_balance_para
  * Compared with the three calls in a row, the router kernel stores each 256-token tile's loads
  * in the dispatch workspace (the dispatch does not count them again; bf16 inputs with
  * d % 64 == 0 only, else a counting pass runs), and the bias update runs inside the dispatch's
- * scan launch.  The update sees `counts` after this batch's loads were added, and changes
+ * scatter launch.  The update sees `counts` after this batch's loads were added, and changes
  * `bias` only after the router kernel has read it, so the next step routes with the new bias.
  * A training loop with one batch per optimizer step sets ELB_ACCUMULATE_COUNTS and
  * ELB_CLEAR_COUNTS and never resets `counts` itself (they must start at zero).

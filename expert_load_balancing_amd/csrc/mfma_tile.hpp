@@ -11,7 +11,8 @@
 // all 256 A rows, i.e. 8 x NB accumulators of 32 x 32 (NB = 2: a 256 x 256 tile in 256 AGPRs;
 // NB = 1: a 256 x 128 tile, for batches too small to give every CU a 256-row B tile).  With
 // ES = 2 the workgroup has 8 waves, two per SIMD, and the waves 2 p and 2 p + 1 split those B
-// rows' A rows between them (128 each).  A 32 x 32 MFMA output puts one
+// rows' A rows between them (128 each); with PR as well, only waves 4-7 (one per SIMD) issue
+// the DMAs, and waves 0-3 only read LDS and multiply.  A 32 x 32 MFMA output puts one
 // B row per lane column: lane l holds column l % 32 of its block, and accumulator r holds A row
 // 8 (r / 4) + 4 (l / 32) + (r % 4).
 //

@@ -216,7 +216,9 @@ struct KRows {
 template <int AUX_A, int AUX_B, class LA = RowsK, class LB = RowsK, int NB = kNB, int ES = 1, bool PR = false>
 struct Stream {
   static_assert(NB == kNB || (NB == 1 && LB::kReads == 1), "a 128-row B tile is laid out rows-contiguous-in-k");
-  static_assert(ES == 1 || (ES == 2 && LA::kReads == 1 && LB::kReads == 1), "the 8-wave split: rows-contiguous-in-k");
+  // Eight waves sharing the DMAs split a slot over 8: only rows-contiguous layouts lay out that way
+  // (with PR four waves issue them, as in the 4-wave tile).
+  static_assert(ES == 1 || (ES == 2 && (PR || (LA::kReads == 1 && LB::kReads == 1))), "the 8-wave DMA split");
   static_assert(!PR || ES == 2, "DMA-issuing waves need a second wave per SIMD");
   static constexpr int kWavesS = kWaves * ES;
   static constexpr int kMBw = kMB / ES;  // A blocks per wave

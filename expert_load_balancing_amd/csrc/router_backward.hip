@@ -362,25 +362,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0) & ~(15 << 8));
 }
 
-// Store a 256 x 256 fp32 tile (acc of the streaming product, rows m of A, columns n of B)
-// through the wave's own LDS slot, one 32-column block at a time ([256 rows][32 columns] fp32 =
-// 32 KiB), then in 16-byte pieces, 8 rows x 128 bytes per store.  Stores m < c_rows, n < c_cols
-// (c_cols % 4 == 0), row stride ldc.
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[kMB][kNB], float* stage, float* C, int64_t ldc,
-                                           int64_t m0, int64_t n0, int64_t c_rows, int64_t c_cols, int wave,
-                                           int lane) {
+// Store one wave's blocks of the fp32 product (acc of the streaming product: MBW blocks of 32 A
+// rows from row m0, kNB blocks of 32 B rows from column n0) through the wave's own LDS stage, one
+// 32-column block at a time ([32 MBW rows][32 columns] fp32), then in 16-byte pieces, 8 rows x
+// 128 bytes per store.  Stores m < c_rows, n < c_cols (c_cols % 4 == 0), row stride ldc.
+template <int MBW>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[MBW][kNB], float* stage, float* C, int64_t ldc,
+                                           int64_t m0, int64_t n0, int64_t c_rows, int64_t c_cols, int lane) {
   const int h = lane >> 5;
   const int l32 = lane & 31;
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
 #pragma unroll
-    for (int mb = 0; mb < kMB; ++mb)
+    for (int mb = 0; mb < MBW; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) stage[(mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) * 32 + l32] = acc[mb][nb][r];
     wave_lds_sync();
-    const int64_t n = n0 + wave * kRowsWave + nb * 32 + (lane & 7) * 4;
+    const int64_t n = n0 + nb * 32 + (lane & 7) * 4;
 #pragma unroll 8
-    for (int q = 0; q < 32; ++q) {
+    for (int q = 0; q < 4 * MBW; ++q) {
       const int row = 8 * q + (lane >> 3);
       const int64_t m = m0 + row;
       const f32x4 v = *reinterpret_cast<const f32x4*>(stage + row * 32 + (lane & 7) * 4);
@@ -393,8 +393,10 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[kMB][kNB], float*
 // part[z][m][n0 + n] = sum over tokens t of range z of dZ[t][m] X[t][n0 + n]   (m, n < 256).
 // Range z covers 64-token stages [Q z / S, Q (z + 1) / S) (Q = ceil(T / 64), S = splits).  The
 // workgroups that share a range run on one XCD (a linear id L runs on XCD L % 8), so its dZ rows
-// come from HBM once into that XCD's L2 and serve all n_col column tiles there.
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void dw_kernel(
+// come from HBM once into that XCD's L2 and serve all n_col column tiles there.  8 waves, two per
+// SIMD: wave w holds dW rows 128 (w % 2) .. + 127 of columns 64 (w / 2) .. + 63; waves 4-7 issue
+// the DMAs, waves 0-3 only read LDS and multiply.
+__global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dw_kernel(
     const uint16_t* __restrict__ dz, const uint16_t* __restrict__ x, int64_t T, int d, int64_t Q, int splits,
     int n_col, float* __restrict__ part) {
   __shared__ __attribute__((aligned(1024))) unsigned char xs0[kSlot], xs1[kSlot], xs2[kSlot];
@@ -413,14 +415,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int64_t t1 = s1 * kBK < T ? s1 * kBK : T;
   const int64_t n0 = (int64_t)col * kRowsB;
   const uint32_t xrow = (uint32_t)d * 2u;
-  Stream<kAuxCached, kAuxStream, KRows, KRows> st;
+  Stream<kAuxCached, kAuxStream, KRows, KRows, kNB, 2, true> st;
   st.init(dz + t0 * kRowsA, (uint32_t)(t1 - t0) * (uint32_t)(kRowsA * 2), (uint32_t)(kRowsA * 2), x + t0 * d + n0,
           (uint32_t)((t1 - t0) * xrow - 2 * n0), xrow, (int)(s1 - s0), wave, lane, Slots{xs0, xs1, xs2, ws0, ws1});
   st.prologue();
-  f32x16 acc[kMB][kNB];
+  f32x16 acc[kMB / 2][kNB];
   st.run(acc, wave, lane);
-  float* const stage = reinterpret_cast<float*>(wave == 0 ? xs0 : wave == 1 ? xs1 : wave == 2 ? xs2 : ws0);
-  store_tile(acc, stage, part + (int64_t)z * kRowsA * d, d, 0, n0, kRowsA, d, wave, lane);
+  // Stage: 16 KiB half (w & 1) of slot w / 2.
+  unsigned char* const sl = (wave >> 1) == 0 ? xs0 : (wave >> 1) == 1 ? xs1 : (wave >> 1) == 2 ? xs2 : ws0;
+  float* const stage = reinterpret_cast<float*>(sl + (wave & 1) * 16384);
+  store_tile<kMB / 2>(acc, stage, part + (int64_t)z * kRowsA * d, d, (wave & 1) * 128, n0 + (wave >> 1) * kRowsWave,
+                      kRowsA, d, lane);
 }
 
 // out[i] = sum_{s < S} part[s * stride + i], in order s = 0, 1, ... (0 for S = 0); n4 float4s.
@@ -497,7 +502,7 @@ hipError_t launch_router_backward(const BackwardArgs& a, const BackwardPlan& p, 
   }
   if (a.dw == nullptr) return err;
   if (a.T > 0) {
-    err = launch(dw_kernel, dim3((unsigned)(p.n_col * p.splits)), dim3(kThreads), 0, s, (const uint16_t*)p.dz,
+    err = launch(dw_kernel, dim3((unsigned)(p.n_col * p.splits)), dim3(2 * kThreads), 0, s, (const uint16_t*)p.dz,
                  (const uint16_t*)a.x, a.T, a.d, p.Q, p.splits, p.n_col, p.part);
     if (err != hipSuccess) return err;
   }

@@ -8,9 +8,10 @@ step, T = 65536 tokens, d = 3072, N_r = 256, K = 4, 32 Zipf clusters (synthetic)
     python bench.py [--steps K] [--warmup W] [--workload large] [--no-cpu]
 
 Prints one JSON line: throughput, the router kernel's roofline position (algorithmic HBM
-bytes over its own average duration, measured with HIP events on its stream), HBM traffic
-from the committed rocprofv3 counter summary when it matches the current kernel source,
-and the CPU oracle timed on the host on the same workload.
+bytes over its average duration across 200 back-to-back launches on the same stream, between
+fence-free HIP events bound to the kernels), HBM traffic from the committed rocprofv3 counter
+summary when it matches the current kernel source, the dispatch's achieved bytes, the rows
+beside the hot path, and the CPU oracle timed on the host on the same workload.
 """
 
 from __future__ import annotations

@@ -74,7 +74,8 @@ hipError_t launch_mark(hipEvent_t ev, hipStream_t stream);
 
 bool router_mfma_applies(const RouterArgs& a);
 // true: the MFMA router runs 256-token tiles for T tokens and fills the dispatch's loads table;
-// false: 128-token tiles (batches of at most 128 tokens per CU), and the dispatch counts itself.
+// false: 128-token tiles (batches of at most 128 tokens per CU; 64-token tiles for at most 64
+// per CU), and the dispatch counts itself.
 bool router_mfma_full_tile(int64_t T);
 hipError_t launch_router_mfma(const RouterArgs& a, hipStream_t stream);
 hipError_t launch_router_generic(const RouterArgs& a, hipStream_t stream);

@@ -212,20 +212,25 @@ struct KRows {
 // elements are contracted (nkb >= 1).  PR (with ES = 2): only waves kWaves .. 2 kWaves - 1 (one
 // per SIMD) issue the DMAs, twice their share each; the other wave of each SIMD only reads LDS
 // and issues MFMAs, so no DMA that waits for room in the vector memory pipeline ever holds up
-// its MFMAs (a wave issues in order).
-template <int AUX_A, int AUX_B, class LA = RowsK, class LB = RowsK, int NB = kNB, int ES = 1, bool PR = false>
+// its MFMAs (a wave issues in order).  TG: token groups (waves / ES); TG = 2 (with ES = 2, NB = 1)
+// makes a 4-wave tile of 64 B rows, for batches too small to give every CU even 128 B rows.
+template <int AUX_A, int AUX_B, class LA = RowsK, class LB = RowsK, int NB = kNB, int ES = 1, bool PR = false,
+          int TG = kWaves>
 struct Stream {
   static_assert(NB == kNB || (NB == 1 && LB::kReads == 1), "a 128-row B tile is laid out rows-contiguous-in-k");
   // Eight waves sharing the DMAs split a slot over 8: only rows-contiguous layouts lay out that way
   // (with PR four waves issue them, as in the 4-wave tile).
   static_assert(ES == 1 || (ES == 2 && (PR || (LA::kReads == 1 && LB::kReads == 1))), "the 8-wave DMA split");
-  static_assert(!PR || ES == 2, "DMA-issuing waves need a second wave per SIMD");
-  static constexpr int kWavesS = kWaves * ES;
+  static_assert(!PR || (ES == 2 && TG == kWaves), "DMA-issuing waves need a second wave per SIMD");
+  static_assert(TG == kWaves || (TG == 2 && ES == 2 && NB == 1 && LA::kReads == 1 && LB::kReads == 1),
+                "the 64-row B tile: 4 waves, rows-contiguous-in-k");
+  static constexpr int kWavesS = TG * ES;
   static constexpr int kMBw = kMB / ES;  // A blocks per wave
-  // DMA instructions per issuing wave per stage (1 KiB each): A's 256 rows, B's 128 NB rows,
-  // over the waves that issue them.
-  static constexpr int kDmaA = PR ? kDma : kDma / ES;
-  static constexpr int kDmaB = PR ? kDma * NB / kNB : kDma * NB / kNB / ES;
+  // Waves that issue the DMAs, and DMA instructions per issuing wave per stage (1 KiB each): A's
+  // 256 rows, B's 32 TG NB rows (128-byte row segments), over the waves that issue them.
+  static constexpr int kSharers = PR ? kWaves : kWavesS;
+  static constexpr int kDmaA = kDma * kWaves / kSharers;
+  static constexpr int kDmaB = TG * NB * 4 / kSharers;
   // VMEM instructions a wave issues after the DMAs of stage j's A rows, when it must have stage
   // j: the B DMAs of the same iteration, then (kPW - 1) full iterations.
   static constexpr int kBudget = kDmaB + (kDmaA + kDmaB) * (kPW - 1);
@@ -247,11 +252,10 @@ struct Stream {
     sl = slots;
     issues = !PR || wave >= kWaves;
     const int dw = PR ? (wave >= kWaves ? wave - kWaves : 0) : wave;  // the wave's share of the DMAs
-    constexpr int kSharers = PR ? kWaves : kWavesS;
 #pragma unroll
     for (int i = 0; i < kDmaA; ++i) voa[i] = LA::dma_off(dw, lane, i, a_row_bytes, 256 / kSharers);
 #pragma unroll
-    for (int i = 0; i < kDmaB; ++i) vob[i] = LB::dma_off(dw, lane, i, b_row_bytes, 128 * NB / kSharers);
+    for (int i = 0; i < kDmaB; ++i) vob[i] = LB::dma_off(dw, lane, i, b_row_bytes, 32 * TG * NB / kSharers);
     wave_off_a = (uint32_t)dw * (kDmaA * 1024);  // A: 64 rows x 128 B or 16 rows x 512 B
     wave_off_b = (uint32_t)dw * (kDmaB * 1024);
     a_stage = LA::stage_bytes(a_row_bytes);

@@ -231,8 +231,8 @@ __device__ __forceinline__ void epilogue_split(const f32x16 (&acc)[kMB / 2][NB],
 
 // NB: 32-token blocks per wave pair (tile of 128 NB tokens).  8 waves, two per SIMD: each pair
 // shares a token range, and each wave of it holds 128 of the 256 experts.
-template <int K, bool FULL, bool EXTRA, int NB>
-__global__ __launch_bounds__(kThreads * 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void router_mfma_kernel(
+template <int K, bool FULL, bool EXTRA, int NB, int TG>
+__global__ __launch_bounds__(TG * 128) __attribute__((amdgpu_waves_per_eu(2, 2))) void router_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const float* __restrict__ bias, int64_t T, int d,
     int n_experts, int normalize, int32_t* __restrict__ idx_out, float* __restrict__ gates_out,
     int32_t* __restrict__ counts, float* __restrict__ logits, float* __restrict__ lse,
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(kThreads * 2) __attribute__((amdgpu_waves_per_eu(2,
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps LDS bases in SGPRs
-  constexpr int kTok = 4 * 32 * NB;  // tokens per workgroup
+  constexpr int kTok = TG * 32 * NB;  // tokens per workgroup
   const int64_t row0 = (int64_t)blockIdx.x * kTok;
   const int rows = (int)(T - row0 < kTok ? T - row0 : kTok);
 
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(kThreads * 2) __attribute__((amdgpu_waves_per_eu(2,
 
   // ---- operand streams: start the DMA ring (A = weights, B = this tile's tokens) ----
   const uint32_t row_bytes = (uint32_t)d * 2u;
-  Stream<kAuxCached, kAuxStream, RowsK, RowsK, NB, 2, true> st;
+  Stream<kAuxCached, kAuxStream, RowsK, RowsK, NB, 2, TG == kWaves, TG> st;
   st.init(w, (uint32_t)n_experts * row_bytes, row_bytes, x + row0 * d, (uint32_t)rows * row_bytes, row_bytes,
           d / kBK, wave, lane, Slots{xs0, xs1, xs2, ws0, ws1});
   st.prologue();
@@ -285,24 +285,27 @@ __global__ __launch_bounds__(kThreads * 2) __attribute__((amdgpu_waves_per_eu(2,
   }
 }
 
-template <int K, bool FULL, int NB>
+template <int K, bool FULL, int NB, int TG>
 hipError_t launch_kfn(const RouterArgs& a, hipStream_t stream) {
   const int normalize = (a.flags & ELB_GATES_RAW) ? 0 : 1;
-  constexpr int kTok = 4 * 32 * NB;
+  constexpr int kTok = TG * 32 * NB;
   const dim3 grid((unsigned)((a.T + kTok - 1) / kTok));
   int32_t* const loads = NB == kNB ? a.tile_loads : nullptr;
   if (a.logits != nullptr || a.lse != nullptr)
-    return launch_timed(router_mfma_kernel<K, FULL, true, NB>, grid, dim3(kThreads * 2), 0, stream, nullptr, a.ev_stop,
+    return launch_timed(router_mfma_kernel<K, FULL, true, NB, TG>, grid, dim3(TG * 128), 0, stream, nullptr, a.ev_stop,
                         (const uint16_t*)a.x, (const uint16_t*)a.w, a.bias, a.T, a.d, a.n_experts, normalize, a.idx,
                         a.gates, a.counts, a.logits, a.lse, loads, a.loads_stride);
-  return launch_timed(router_mfma_kernel<K, FULL, false, NB>, grid, dim3(kThreads * 2), 0, stream, nullptr, a.ev_stop,
+  return launch_timed(router_mfma_kernel<K, FULL, false, NB, TG>, grid, dim3(TG * 128), 0, stream, nullptr, a.ev_stop,
                       (const uint16_t*)a.x, (const uint16_t*)a.w, a.bias, a.T, a.d, a.n_experts, normalize, a.idx,
                       a.gates, a.counts, a.logits, a.lse, loads, a.loads_stride);
 }
 
 template <int K, bool FULL>
 hipError_t launch_kf(const RouterArgs& a, hipStream_t stream) {
-  return router_mfma_full_tile(a.T) ? launch_kfn<K, FULL, kNB>(a, stream) : launch_kfn<K, FULL, 1>(a, stream);
+  if (router_mfma_full_tile(a.T)) return launch_kfn<K, FULL, kNB, kWaves>(a, stream);
+  // Half-size batches: 128-token tiles; below that 64-token tiles, so every CU still gets one.
+  return a.T > (int64_t)(kTile / 4) * kCus ? launch_kfn<K, FULL, 1, kWaves>(a, stream)
+                                           : launch_kfn<K, FULL, 1, 2>(a, stream);
 }
 
 template <int K>

@@ -168,8 +168,9 @@ elb_status elb_smebu_update(int32_t* counts, int32_t n_experts, elb_balance_para
  * ELB_CLEAR_COUNTS and never resets `counts` itself (they must start at zero).
  * offsets, perm and inv_perm all NULL: no dispatch (workspace is then not used); the update,
  * if any, runs as its own launch after the router kernel.
- * The MFMA router takes 128-token tiles for batches of at most 128 x 256 tokens (so that every
- * compute unit gets a tile); the dispatch then counts the loads itself.
+ * The MFMA router takes 128-token tiles for batches of at most 128 x 256 tokens and 64-token
+ * tiles for at most 64 x 256 (so that every compute unit gets a tile); the dispatch then counts
+ * the loads itself.
  * timing: NULL, or two hipEvent_t (either may be NULL) that bracket the router kernel: the
  * first takes the end time stamp of an empty one-wave kernel launched right before it, the
  * second the router kernel's own end (both through hipExtLaunchKernel; with T == 0 the empty

@@ -179,7 +179,7 @@ def test_route_step_without_dispatch_matches():
         log(f"T={T}: identical with and without dispatch")
 
 
-@pytest.mark.parametrize("T", [32768, 32769, 40000])
+@pytest.mark.parametrize("T", [16384, 16385, 32768, 32769, 40000])
 def test_route_step_dispatch_at_tile_switch(T):
     """The fused step's dispatch on either side of the tile-size switch: 128-token router tiles
     (the dispatch counts the loads itself) and 256-token tiles with a ragged tail (the router

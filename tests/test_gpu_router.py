@@ -52,13 +52,17 @@ def test_router_matches_oracle(T, d, n_e, k, kind, kernel):
 
 
 @pytest.mark.parametrize("T", [
+    1000,    # 64-token tiles: 16 of them, ragged tail of 40
+    16383,   # 64-token tiles: 256 of them, ragged tail of 63
+    16384,   # the largest batch on 64-token tiles
+    16385,   # the smallest on 128-token tiles: 129 tiles, the last holding one token
     32767,   # 128-token tiles: 256 of them, ragged tail of 127
     32768,   # the largest batch on 128-token tiles
     32769,   # the smallest on 256-token tiles: 129 tiles, the last holding one token
     40000,   # 256-token tiles with a ragged tail of 64
 ])
 def test_router_tile_sizes(T):
-    """Both MFMA tile sizes and the switch between them, with ragged tails."""
+    """The three MFMA tile sizes and the switches between them, with ragged tails."""
     log(f"router tile sizes T={T}")
     wl, x, w, b = make(T, 256, 256, 4, kind="clusters")
     idx, gates, counts, logits = run(x, w, b, 4)
@@ -68,10 +72,11 @@ def test_router_tile_sizes(T):
     log(f"  ties={rep.ties} (mismatched {rep.tie_mismatch}) gate rel err={rep.max_gate_rel:.2e}")
 
 
-@pytest.mark.parametrize("T,n_e,k", [(33000, 200, 8), (40000, 64, 1), (36000, 256, 3)])
+@pytest.mark.parametrize("T,n_e,k", [(33000, 200, 8), (40000, 64, 1), (36000, 256, 3),
+                                     (9000, 200, 8), (5000, 64, 1), (16000, 256, 3), (20000, 100, 5)])
 def test_router_full_tile_shapes(T, n_e, k):
-    """The full (8-wave) tile with padded experts (some waves hold none), every K, and the
-    log-sum-exp combined across the two waves of a token."""
+    """Each tile size (256 tokens on 8 waves; 128 on 8; 64 on 4) with padded experts (some waves
+    hold none), several K, and the log-sum-exp combined across the two waves of a token."""
     log(f"router full tile T={T} N_r={n_e} K={k}")
     wl, x, w, b = make(T, 128, n_e, k, kind="clusters")
     res = elb.router_forward(to_dev(x), to_dev(w), to_dev(b), k, want_logits=True, want_lse=True)

@@ -38,6 +38,8 @@ def run(x, w, b, k, **kw):
     (2048, 1024, 256, 4, "clusters"),
     (300, 8192, 256, 4, "clusters"),   # wide rows: 16 KiB per token
     (200, 128, 1, 1, "iid"),           # a single expert
+    (1000, 128, 8, 8, "clusters"),     # K = N_r: every expert chosen, ordered by s + b
+    (333, 64, 255, 7, "iid"),          # one padded expert slot, odd K
 ])
 @pytest.mark.parametrize("kernel", ["mfma", "generic"])
 def test_router_matches_oracle(T, d, n_e, k, kind, kernel):

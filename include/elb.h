@@ -103,8 +103,10 @@ typedef struct {
  *            section "Precision Fallbacks, Loss Stabilization, and MaxVio ...").
  * Supported: 0 <= T, T * k < 2^31; 1 <= k <= min(8, n_experts); n_experts <= 256;
  * d >= 1 with every row 16-byte aligned (d % 8 == 0 for bf16, d % 4 == 0 for fp32);
- * x and w 16-byte aligned.  bf16 inputs with d % 64 == 0 run on the MFMA kernel.
- * Inputs must be finite.  Errors: ELB_ERR_NULL, ELB_ERR_SHAPE, ELB_ERR_ALIGN,
+ * x and w 16-byte aligned.  bf16 inputs with d % 64 == 0 run on the MFMA kernel, which ranks
+ * s + b by keys that resolve differences down to 2^-15 (1 + max b - min b) (about 3e-5 for the
+ * biases SMEBU produces; closer candidates go to the lower expert index); the generic kernel
+ * (ELB_FORCE_GENERIC) compares s + b exactly in fp32.  Inputs must be finite.  Errors: ELB_ERR_NULL, ELB_ERR_SHAPE, ELB_ERR_ALIGN,
  * ELB_ERR_UNSUPPORTED (dtype or flag), ELB_ERR_LAUNCH.
  */
 elb_status elb_router_forward(const void* x, int32_t dtype, int64_t T, int32_t d, const void* w,

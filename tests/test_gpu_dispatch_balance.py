@@ -13,7 +13,7 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("T,k,n_e,skew", [
     (1, 1, 16, 0.0), (1, 4, 256, 0.0), (257, 4, 256, 0.0), (1000, 2, 16, 1.5), (4096, 4, 256, 1.2),
-    (65536, 4, 256, 1.1), (70001, 3, 200, 0.8), (262144, 4, 256, 1.1), (5, 8, 8, 0.0),
+    (65536, 4, 256, 1.1), (65535, 4, 256, 0.0), (65280, 2, 256, 1.0), (65537, 4, 256, 0.5), (70001, 3, 200, 0.8), (262144, 4, 256, 1.1), (5, 8, 8, 0.0),
     (1300, 8, 64, 1.0), (513, 5, 256, 0.0), (777, 6, 100, 2.0), (2049, 7, 9, 0.0), (300, 1, 1, 0.0),
 ])
 def test_dispatch_matches_oracle(T, k, n_e, skew):
@@ -54,10 +54,11 @@ def test_dispatch_concentrated_and_repeated_ids():
         check_dispatch(offs.cpu().numpy(), perm.cpu().numpy(), inv.cpu().numpy(), idx, n_e)
 
 
-def test_dispatch_without_inverse_and_reused_workspace():
+@pytest.mark.parametrize("T", [9000, 8900, 70000])  # 36 tiles; 35 (one padding column); 274
+def test_dispatch_without_inverse_and_reused_workspace(T):
     rng = np.random.default_rng(3)
-    idx = rng.integers(0, 256, size=(9000, 4)).astype(np.int32)
-    need = elb.dispatch_workspace_bytes(9000, 4, 256)
+    idx = rng.integers(0, 256, size=(T, 4)).astype(np.int32)
+    need = elb.dispatch_workspace_bytes(T, 4, 256)
     ws = torch.full((need,), 0xAB, dtype=torch.uint8, device="cuda")  # garbage contents on entry
     for _ in range(2):
         offs, perm, inv = elb.router_dispatch(to_dev(idx), 256, workspace=ws, want_inv=False)

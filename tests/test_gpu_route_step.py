@@ -179,11 +179,11 @@ def test_route_step_without_dispatch_matches():
         log(f"T={T}: identical with and without dispatch")
 
 
-@pytest.mark.parametrize("T", [16384, 16385, 32768, 32769, 40000])
+@pytest.mark.parametrize("T", [16384, 16385, 32768, 32769, 40000, 65535, 65536, 65537])
 def test_route_step_dispatch_at_tile_switch(T):
     """The fused step's dispatch on either side of the tile-size switch: 128-token router tiles
     (the dispatch counts the loads itself) and 256-token tiles with a ragged tail (the router
-    fills the loads table)."""
+    fills the loads table), up to the large workload's 65,536 tokens and one token past it."""
     wl = datagen.WORKLOADS["large"].replace(T=T, d=256, seed=T + 3, n_clusters=8)
     x, w, b = datagen.tokens(wl), datagen.router_weight(wl), datagen.initial_bias(wl)
     step = elb.RouterStep(to_dev(w), to_dev(b), torch.zeros(wl.n_experts, device="cuda"), wl.k, T, update=False)

@@ -98,6 +98,7 @@ def test_dispatch_workspace_size(lib):
     (dict(offsets=None), NULL), (dict(idx=None), NULL), (dict(perm=None), NULL), (dict(ws=None), NULL),
     (dict(n=0), SHAPE), (dict(n=257), SHAPE), (dict(k=0), SHAPE), (dict(T=-5), SHAPE),
     (dict(ws_bytes=16), WORKSPACE), (dict(ws=FAKE + 4), ALIGN), (dict(perm=FAKE + 2), ALIGN),
+    (dict(T=(1 << 31) // 8, k=8, ws_bytes=1 << 31), SHAPE),  # T * k = 2^31: past the int32 positions
 ])
 def test_router_dispatch_rejects(lib, kw, want):
     a = dict(idx=FAKE, T=4096, k=4, n=256, ws=FAKE, ws_bytes=1 << 20, offsets=FAKE, perm=FAKE, inv=None)

@@ -136,3 +136,28 @@ def sample_rows(T: int, n: int, seed: int, extra=()) -> np.ndarray:
     rows.update([0, T - 1] + list(range(max(0, T - 37), T)))
     rows.update(int(r) for r in extra)
     return np.array(sorted(rows), dtype=np.int64)
+
+
+def check_dispatch_device(offs: torch.Tensor, perm: torch.Tensor, inv: torch.Tensor, flat: torch.Tensor,
+                          n_experts: int, chunk: int = 1 << 27) -> None:
+    """The stable counting sort of the flat ids `flat` checked on the device, in chunks, for sizes
+    the host cannot sort: bucket sizes = id histogram, perm[inv] = identity, ids non-decreasing
+    along perm, flat positions ascending inside a bucket.  Together these leave exactly one perm."""
+    n = flat.numel()
+    hist = torch.zeros(n_experts, dtype=torch.int64, device=flat.device)
+    for lo in range(0, n, chunk):
+        hist += torch.bincount(flat[lo:lo + chunk].long(), minlength=n_experts)
+    o = offs.long()
+    assert o[0].item() == 0 and o[-1].item() == n
+    assert torch.equal(o[1:] - o[:-1], hist), "bucket sizes differ from the id histogram"
+    for lo in range(0, n, chunk):
+        hi = min(lo + chunk, n)
+        back = perm[inv[lo:hi].long()].long()
+        assert torch.equal(back, torch.arange(lo, hi, device=flat.device)), f"perm[inv] differs near {lo}"
+    for lo in range(0, n, chunk):  # each chunk together with the first entry of the next
+        p = perm[lo:min(lo + chunk + 1, n)].long()
+        e = flat[p]
+        de = e[1:] - e[:-1]
+        assert bool((de >= 0).all()), f"ids decrease along perm near {lo}"
+        same = de == 0
+        assert bool((p[1:][same] > p[:-1][same]).all()), f"unstable bucket near {lo}"

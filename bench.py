@@ -79,6 +79,14 @@ class TimingEvent:
             TimingEvent._hip.hipEventDestroy(ctypes.c_void_p(self.cuda_event))
 
 
+def router_kernel_name(T: int, n_e: int, k: int) -> str:
+    """The MFMA router instantiation a forward of T tokens runs, as the profiler names it:
+    <K, all 256 experts, no logits/lse copy, 32-token blocks per wave pair, waves / 2> with the
+    256-token tile above 128 x 256 tokens, the 128-token tile above 64 x 256, else the 64-token."""
+    nb, tg = (2, 4) if T > 128 * 256 else (1, 4) if T > 64 * 256 else (1, 2)
+    return f"router_mfma_kernel<{k}, {'true' if n_e == 256 else 'false'}, false, {nb}, {tg}>"
+
+
 def dispatch_alg_bytes(T: int, n_e: int, k: int) -> int:
     """HBM bytes the dispatch must move: idx in once, perm and inv out, offsets out."""
     return T * k * 4 * 3 + (n_e + 1) * 4
@@ -367,7 +375,7 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else round(traffic),
-                     "kernel": "router_mfma_kernel<4>", "alg_bytes_per_launch": alg, "launches_timed": n_solo,
+                     "kernel": router_kernel_name(T, n_e, k), "alg_bytes_per_launch": alg, "launches_timed": n_solo,
                      "kernel_us": round(router_ms * 1e3, 2),
                      "mfma_tflops": round(tflops, 1), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)},
         "breakdown_us": {"step": round(ms * 1e3, 2), "router_back_to_back": round(router_ms * 1e3, 2)},

@@ -29,6 +29,13 @@ def test_router_alg_bytes_large_workload():
     assert bench.router_alg_bytes(T, d, n_e, k) == 406_325_248
 
 
+def test_router_kernel_name_follows_the_tile_switch():
+    # The names the profiler prints for the three tiles (see profiles/).
+    assert bench.router_kernel_name(65536, 256, 4) == "router_mfma_kernel<4, true, false, 2, 4>"
+    assert bench.router_kernel_name(32768, 256, 4) == "router_mfma_kernel<4, true, false, 1, 4>"
+    assert bench.router_kernel_name(16384, 200, 2) == "router_mfma_kernel<2, false, false, 1, 2>"
+
+
 def test_dispatch_alg_bytes_large_workload():
     # idx in (16 B per token at K = 4), perm and inv out (32 B per token), offsets out.
     T, n_e, k = 65536, 256, 4
@@ -47,7 +54,7 @@ def _counter_csv(path, counter, rows):
                             "Counter_Value": v})
 
 
-ROUTER = "void elb::(anonymous namespace)::router_mfma_kernel<4, true, false, 2>(unsigned short const*, ...)"
+ROUTER = "void elb::(anonymous namespace)::router_mfma_kernel<4, true, false, 2, 4>(unsigned short const*, ...)"
 
 
 def test_summarize_traffic_scales_and_averages_the_last_launches(tmp_path):

@@ -38,6 +38,16 @@ MUTANTS = [
     ("balance.py", "m_new = beta * m + (1.0 - beta) * db\n", "m_new = beta * m + (1.0 - beta) * db_raw\n",
      "re-centre after momentum"),
     ("balance.py", "db = gamma * np.sign(nbar - n)", "db = gamma * np.sign(nbar - n + 0.5)", "sign(0) taken as +1"),
+    ("balance.py", 'vt = np.tanh(kappa * v) if mode == "smebu" else v', "vt = np.tanh(kappa * v)",
+     "linear mode through tanh"),
+    ("balance.py", "return BalanceStep(b_new, m.copy(), db, db.copy())",
+     "return BalanceStep(b_new, beta * m + (1.0 - beta) * db, db, db.copy())", "sign mode moves the momentum"),
+    ("balance.py", "nbar = n.sum() / len(n)\n    if mode", "nbar = n.sum() / (len(n) - 1)\n    if mode",
+     "mean load over N_r - 1"),
+    ("loads.py", "offsets = np.concatenate([[0], np.cumsum(counts)])",
+     "offsets = np.concatenate([np.cumsum(counts), [counts.sum()]])", "inclusive bucket offsets"),
+    ("loads.py", "inv[perm] = np.arange(len(perm), dtype=np.int64)", "inv[:] = perm", "inv taken as perm"),
+    ("zloss.py", "np.exp(z - zmax).sum(axis=1", "np.exp(z - zmax).mean(axis=1", "log-mean-exp"),
     ("loads.py", 'np.argsort(flat, kind="stable")', 'np.argsort(flat, kind="quicksort")', "unstable dispatch"),
     ("loads.py", "ratio = float(\"inf\") if nmin == 0 else nmax / nmin",
      "ratio = float(\"inf\") if nmin == 0 else nmax / nbar", "MaxVio over the mean"),

@@ -22,6 +22,7 @@ MUTANTS = [
      "gates from s + b"),
     ("router.py", 'order = np.argsort(-q, axis=1, kind="stable")', 'order = np.argsort(q, axis=1, kind="stable")[:, ::-1]',
      "ties to the higher index"),
+    ("router.py", "q = s + b[None, :]", "q = s - b[None, :]", "bias subtracted"),
     ("router.py", "return widen(x) @ widen(w).T", "return widen(x)[:, :-1] @ widen(w)[:, :-1].T", "dropped last term"),
     ("router.py", "1.0 / (1.0 + np.exp(-z))", "1.0 / (1.0 + np.exp(z))", "sigmoid sign"),
     ("router.py", "gap = q[rows, order[:, k - 1]] - q[rows, order[:, k]]",
@@ -68,6 +69,8 @@ MUTANTS = [
      "z-loss factor 2 dropped"),
     ("backward.py", "return RouterGrads(dz=dz, dx=dz @ w64, dw=dz.T @ x64",
      "return RouterGrads(dz=dz, dx=dz @ w64, dw=dz.T @ x64[::-1]", "tokens reversed in dW"),
+    ("backward.py", "return RouterGrads(dz=dz, dx=dz @ w64,", "return RouterGrads(dz=dz, dx=dz @ w64[::-1],",
+     "expert rows reversed in dX"),
 ]
 
 

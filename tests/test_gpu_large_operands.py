@@ -89,7 +89,7 @@ def test_router_dispatch_moe_ops_and_backward_past_4gib():
     zmax = z.max(axis=1, keepdims=True)
     e = np.exp(z - zmax)
     dz += zc * (2.0 / T) * (zmax + np.log(e.sum(axis=1, keepdims=True))) * e / e.sum(axis=1, keepdims=True)
-    bound = (2.0 ** -8 + 256 * 2.0 ** -24) * (np.abs(dz) @ np.abs(w64))
+    bound = (2.0 ** -8 + 2.0 ** -16 + 256 * 2.0 ** -24) * (np.abs(dz) @ np.abs(w64))
     err = np.abs(dx_h - dz @ w64)
     assert (err <= bound + 1e-30).all(), f"dx sampled: worst {err.max():.3g}"
 

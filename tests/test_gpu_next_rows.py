@@ -8,8 +8,8 @@ Tolerances (derived here, from the arithmetic each kernel does):
   * permute: a copy, bit-exact;
   * combine: K fused multiply-adds in fp32; each rounds once, so
     |y - y_ref| <= (K + 1) 2^-24 sum_j |g_j e_j|; a bf16 output adds the round-to-nearest-even
-    half ulp, 2^-9 |y| (checked against 2^-8 to leave room for the fp32 error), and must equal
-    the bf16 rounding of the fp32 result bit for bit;
+    half ulp, at most 2^-8 of the fp32 value (8 significant bits), i.e. 2^-8 (|y_ref| + that
+    bound), and must equal the bf16 rounding of the fp32 result bit for bit;
   * batched update: per layer, the single-layer bar (1e-6 against the oracle), and bit-identical
     to one elb_smebu_update call per layer.
 """

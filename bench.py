@@ -1,17 +1,20 @@
 """Benchmark: routed tokens/s of the full router step on one MI355X.
 
 One step = router forward (logits, sigmoid, biased Top-4, gates, expert loads) + dispatch
-permutation + SMEBU bias update with MaxVio: one elb_route_step call (three kernels) on one
-stream, inputs resident in HBM.  Default workload: one GPU's micro-batch share of the Large-style
-step, T = 65536 tokens, d = 3072, N_r = 256, K = 4, 32 Zipf clusters (synthetic).
+permutation + SMEBU bias update with MaxVio: one elb_route_step call on one stream, inputs
+resident in HBM.  Default workload: the largest single-GPU batch, T = 262144 tokens, d = 4096,
+N_r = 256, K = 4, 64 Zipf clusters with 5% exact duplicate rows (synthetic).
 
-    python bench.py [--steps K] [--warmup W] [--workload large] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--workload stress] [--no-cpu] [--no-next]
+                    [--no-configs] [--no-loop]
 
-Prints one JSON line: throughput, the router kernel's roofline position (algorithmic HBM
-bytes over its average duration across 200 back-to-back launches on the same stream, between
-fence-free HIP events bound to the kernels), HBM traffic from the committed rocprofv3 counter
-summary when it matches the current kernel source, the dispatch's achieved bytes, the rows
-beside the hot path, and the CPU oracle timed on the host on the same workload.
+Prints one JSON line: throughput over exactly K back-to-back steps, the median of separately
+bracketed steps, the router kernel's roofline position (algorithmic HBM bytes over its average
+duration across back-to-back launches on the same stream, between fence-free HIP events bound
+to the kernels), HBM traffic from the committed rocprofv3 counter summary when it matches the
+current kernel source and size, the dispatch's achieved bytes, the other workloads' step and
+router figures, the 300-step closed loop's MaxVio trajectories for the three balancers, the
+rows beside the hot path, and the CPU oracle timed on the host.
 """
 
 from __future__ import annotations
@@ -20,7 +23,9 @@ import argparse
 import ctypes
 import hashlib
 import json
+import math
 import os
+import statistics
 import sys
 import time
 
@@ -30,6 +35,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, AMD published
 METRIC = "routed tokens/s (logits+top-4+counts+SMEBU) at N_r=256,K=4; % roofline"
+DEFAULT_WORKLOAD = "stress"
+OTHER_CONFIGS = ("tiny", "sign", "large", "loop")
+BALANCERS = ("smebu", "sign", "linear")
+MALL_BYTES = 512 << 20  # rotate at least this many bytes of input copies (the last-level cache is 256 MB)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "router_mfma_traffic.json")
 KERNEL_SOURCES = ["expert_load_balancing_amd/csrc/router_mfma.hip", "expert_load_balancing_amd/csrc/mfma_tile.hpp",
                   "expert_load_balancing_amd/csrc/device_common.hpp"]
@@ -92,9 +101,9 @@ def dispatch_alg_bytes(T: int, n_e: int, k: int) -> int:
     return T * k * 4 * 3 + (n_e + 1) * 4
 
 
-def router_alg_bytes(T: int, d: int, n_e: int, k: int) -> int:
+def router_alg_bytes(T: int, d: int, n_e: int, k: int, elem: int = 2) -> int:
     """HBM bytes the router forward must move: X once, W once, idx + gates out, b in, counts."""
-    return T * (2 * d + 8 * k) + n_e * 2 * d + n_e * 4 + n_e * 4
+    return T * (elem * d + 8 * k) + n_e * elem * d + n_e * 4 + n_e * 4
 
 
 def traffic_from_profile(T: int) -> float | None:
@@ -109,15 +118,16 @@ def traffic_from_profile(T: int) -> float | None:
     return float(rec["traffic_bytes_per_launch"])
 
 
-def summarize_traffic(fetch_csv: str, write_csv: str, copy_mib: int, T: int, launches: int) -> dict:
+def summarize_traffic(fetch_csv: str, write_csv: str, copy_mib: int, T: int, launches: int,
+                      workload: str | None = None) -> dict:
     """HBM bytes per router launch from two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE).
 
     Both counters report KiB per dispatch, summed here over the counter's instances, and are
     averaged over the last `launches` router launches: the back-to-back launches the roofline
     times.  (Inside a step the counters of the router launch also take in the write-back of the
-    permutation the previous step's scatter left in the cache, 2 MiB more.)  Each is scaled by
-    what it reads for the plain device-to-device copy of known size that ``--calibrate-copy``
-    runs in the same program (the copy reads and writes copy_mib MiB).
+    permutation the previous step's scatter left in the cache.)  Each is scaled by what it reads
+    for the plain device-to-device copy of known size that ``--calibrate-copy`` runs in the same
+    program (the copy reads and writes copy_mib MiB).
     """
     import csv
     from collections import defaultdict
@@ -139,41 +149,82 @@ def summarize_traffic(fetch_csv: str, write_csv: str, copy_mib: int, T: int, lau
     f_copy = per_kernel(fetch_csv, "FETCH_SIZE", "copyBuffer", last=3)
     w_copy = per_kernel(write_csv, "WRITE_SIZE", "copyBuffer", last=3)
     f_scale, w_scale = copy_bytes / (f_copy * 1024), copy_bytes / (w_copy * 1024)
-    return {
-        "kernel_source_sha256": kernel_source_hash(), "T": T, "launches_averaged": launches,
+    rec = {"kernel_source_sha256": kernel_source_hash(), "T": T, "launches_averaged": launches}
+    if workload is not None:
+        rec["workload"] = workload
+    rec.update({
         "fetch_kib_per_launch": f_router, "write_kib_per_launch": w_router,
         "copy_mib": copy_mib, "copy_fetch_kib": f_copy, "copy_write_kib": w_copy,
         "fetch_scale": f_scale, "write_scale": w_scale,
         "traffic_bytes_per_launch": f_router * 1024 * f_scale + w_router * 1024 * w_scale,
-    }
+    })
+    return rec
 
 
-def cpu_baseline(wl, x, w, b, m, min_seconds: float = 10.0, max_seconds: float = 30.0) -> dict:
-    """The oracle (untuned) on the whole step of the same workload, repeated for >= min_seconds."""
-    import numpy as np
-    from threadpoolctl import threadpool_limits
+def oracle_threads() -> tuple[int, int]:
+    """(threads for the oracle's BLAS, cores in this process's affinity mask).  The threads are
+    every core of the affinity mask, capped by OMP_NUM_THREADS where the host sets it (the share
+    of the host's cores that belongs to this process's GPU)."""
+    affinity = len(os.sched_getaffinity(0))
+    try:
+        share = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        share = 0
+    return (min(affinity, share) if share > 0 else affinity), affinity
 
+
+def _oracle_step(wl, x, w, b, m):
     import oracle
 
-    cores = min(16, len(os.sched_getaffinity(0)))
-    with threadpool_limits(limits=cores):
+    r = oracle.route(x, w, b, wl.k)
+    n = oracle.expert_loads(r.idx, wl.n_experts)
+    oracle.max_violation(n)
+    if wl.dispatch:
+        oracle.dispatch_permutation(r.idx, wl.n_experts)
+    oracle.balance_step(n, b, m, mode=wl.mode, lam=wl.lam, beta=wl.beta, kappa=wl.kappa, gamma=wl.gamma)
+
+
+def _time_oracle(wl, x, w, b, m, threads: int, min_seconds: float, max_seconds: float) -> tuple[int, float]:
+    from threadpoolctl import threadpool_limits
+
+    with threadpool_limits(limits=threads):
         reps, t0 = 0, time.perf_counter()
         while True:
-            r = oracle.route(x, w, b, wl.k)
-            n = oracle.expert_loads(r.idx, wl.n_experts)
-            oracle.max_violation(n)
-            if wl.dispatch:
-                oracle.dispatch_permutation(r.idx, wl.n_experts)
-            oracle.balance_step(n, b, m, mode=wl.mode, lam=wl.lam, beta=wl.beta, kappa=wl.kappa, gamma=wl.gamma)
+            _oracle_step(wl, x, w, b, m)
             reps += 1
             el = time.perf_counter() - t0
             if el >= min_seconds or el * (reps + 1) / reps > max_seconds:
-                break
-    return {"value": reps * wl.T / el, "unit": "routed tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"the full step of {wl.label} (route + loads + MaxVio"
-                      f"{' + dispatch' if wl.dispatch else ''} + {wl.mode} update), {reps} repetition(s), "
-                      f"fp64 numpy, BLAS threads={cores}",
-            "seconds": round(el, 2)}
+                return reps, el
+
+
+def cpu_baseline(wl, x, w, b, m, min_seconds: float = 10.0, max_seconds: float = 30.0,
+                 single_thread: bool = True) -> dict:
+    """The oracle (untuned) on the whole step of the same workload, repeated for >= min_seconds on
+    all of this process's cores; then, on one thread, bounded samples of the three smaller
+    single-step workloads."""
+    import datagen
+
+    threads, affinity = oracle_threads()
+    reps, el = _time_oracle(wl, x, w, b, m, threads, min_seconds, max_seconds)
+    res = {"value": reps * wl.T / el, "unit": "routed tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"the full step of {wl.label} (route + loads + MaxVio"
+                     f"{' + dispatch' if wl.dispatch else ''} + {wl.mode} update), {reps} repetition(s), "
+                     f"fp64 numpy, BLAS threads={threads}",
+           "seconds": round(el, 2), "affinity_cores": affinity,
+           "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+    if single_thread:
+        one = {}
+        for key, rows in (("tiny", None), ("sign", 2048), ("large", 2048)):
+            swl = datagen.WORKLOADS[key]
+            sx = datagen.tokens(swl)
+            if rows is not None:
+                sx = sx[:rows]
+            n, s = _time_oracle(swl.replace(T=len(sx)), sx, datagen.router_weight(swl), datagen.initial_bias(swl),
+                                datagen.initial_momentum(swl), 1, 2.0, 10.0)
+            one[key] = {"value": round(n * len(sx) / s, 1), "unit": "routed tokens/s", "tokens": len(sx),
+                        "repetitions": n, "seconds": round(s, 2)}
+        res["single_thread"] = one
+    return res
 
 
 def time_events(fn, reps: int, stream, per_call: bool = False) -> float:
@@ -223,6 +274,7 @@ def bench_next_rows(elb, wl, x, w, out, stream, reps: int = 20) -> dict:
     y = torch.empty((T, d), dtype=torch.float32, device=x.device)
     ms_p = time_events(lambda: elb.permute_rows(x, inv, k, out=xp), reps, stream)
     ms_c = time_events(lambda: elb.unpermute_combine(xp, gates, inv, out=y), reps, stream)
+    del xp, y
     # Router backward with the z-loss (recomputed logits, dL/dz, dX = dZ W, dW = dZ^T X).
     dg = torch.randn((T, k), device=x.device)
     ws_b = torch.empty(elb.backward_workspace_bytes(T, d, n_e), dtype=torch.uint8, device=x.device)
@@ -244,14 +296,180 @@ def bench_next_rows(elb, wl, x, w, out, stream, reps: int = 20) -> dict:
     return res
 
 
+class Setup:
+    """One workload on the device: seeded inputs (enough identical token copies, alternated step
+    by step, that no step reads its input out of the last-level cache the previous one filled),
+    and a RouterStep holding its own b, m and output buffers."""
+
+    def __init__(self, elb, wl, dev, host_tokens=None):
+        import numpy as np
+        import torch
+
+        import datagen
+
+        self.wl = wl
+        self.x = datagen.tokens(wl) if host_tokens is None else host_tokens
+        self.w = datagen.router_weight(wl)
+        self.b0, self.m0 = datagen.initial_bias(wl), datagen.initial_momentum(wl)
+
+        def to_dev(a):
+            if a.dtype == np.uint16:
+                return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+            return torch.from_numpy(a).to(dev)
+
+        n_copies = max(2, math.ceil(MALL_BYTES / self.x.nbytes))
+        self.xs = [to_dev(self.x) for _ in range(n_copies)]
+        self.wd, self.bd, self.md = to_dev(self.w), to_dev(self.b0), to_dev(self.m0)
+        self.step = elb.RouterStep(self.wd, self.bd, self.md, wl.k, wl.T, mode=wl.mode, lam=wl.lam, beta=wl.beta,
+                                   kappa=wl.kappa, gamma=wl.gamma, dispatch=wl.dispatch)
+        self.i = 0
+
+    def __call__(self):
+        out = self.step(self.xs[self.i % len(self.xs)])
+        self.i += 1
+        return out
+
+
+def time_steps(s: Setup, steps: int, warmup: int, stream) -> tuple[float, object]:
+    """ms per step over exactly `steps` back-to-back steps (after `warmup`), and the last outputs."""
+    import torch
+
+    for _ in range(warmup):
+        s()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    out = None
+    for _ in range(steps):
+        out = s()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps, out
+
+
+def step_median(s: Setup, reps: int) -> dict:
+    """Each of `reps` steps bracketed on its own: from the end of an empty kernel launched just
+    before the router kernel to the end of the step's last kernel (fence-free events bound to
+    the kernels).  Each interval therefore includes one dispatch gap, a few microseconds."""
+    import torch
+
+    ev = [(TimingEvent(), TimingEvent()) for _ in range(reps)]
+    for a, b in ev:
+        s.step.set_timing(a, None, b)
+        s()
+    s.step.set_timing()
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    return {"median": round(statistics.median(us), 2), "min": round(us[0], 2), "max": round(us[-1], 2),
+            "reps": reps}
+
+
+def router_back_to_back(elb, s: Setup, launches: int) -> float:
+    """The router kernel's average launch duration (ms): `launches` launches of it back to back on
+    the same stream (a step with neither dispatch nor update; the counts accumulate), from the end
+    of an empty kernel launched just before the first to the end of the last.  The events are
+    fence-free and bound to those two kernels, so no marker sits between the launches; the one
+    dispatch gap after the empty kernel is spread over the launches.  (A marker beside every
+    launch would add its own ~5 us dispatch gap to each.)  The clock of a power-limited part
+    wanders over milliseconds, so the launches span about as long as the timed steps do."""
+    import torch
+
+    wl = s.wl
+    solo = elb.RouterStep(s.wd, s.bd, None, wl.k, wl.T, update=False, dispatch=False)
+    t0, t1 = TimingEvent(), TimingEvent()
+    for i in range(2):
+        solo(s.xs[i % len(s.xs)])
+    torch.cuda.synchronize()
+    for i in range(launches):
+        solo.set_timing(t0 if i == 0 else None, t1 if i == launches - 1 else None)
+        solo(s.xs[i % len(s.xs)])
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / launches
+
+
+def roofline_of(wl, router_ms: float) -> dict:
+    elem = 2 if wl.dtype == "bf16" else 4
+    alg = router_alg_bytes(wl.T, wl.d, wl.n_experts, wl.k, elem)
+    achieved = alg / (router_ms * 1e-3) / 1e9
+    tflops = 2.0 * wl.T * wl.d * wl.n_experts / (router_ms * 1e-3) / 1e12
+    return {"achieved": round(achieved, 1), "frac": round(achieved / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": alg,
+            "kernel_us": round(router_ms * 1e3, 2), "mfma_tflops": round(tflops, 1),
+            "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)}
+
+
+def bench_config(elb, key: str, dev, stream, steps: int, launches: int) -> dict:
+    """Step and router figures of one of the other workloads (one step of the closed-loop one)."""
+    import datagen
+
+    wl = datagen.WORKLOADS[key]
+    s = Setup(elb, wl, dev)
+    ms, _ = time_steps(s, steps, max(5, steps // 5), stream)
+    med = step_median(s, max(50, steps))
+    res = {"workload": wl.label, "routed_tokens_per_s": round(wl.T / (ms * 1e-3), 1), "step_us": round(ms * 1e3, 2),
+           "step_us_median": med["median"]}
+    if wl.dtype == "bf16":
+        r = roofline_of(wl, router_back_to_back(elb, s, launches))
+        res.update({"router_us": r["kernel_us"], "router_frac": r["frac"], "router_GBps": r["achieved"],
+                    "kernel": router_kernel_name(wl.T, wl.n_experts, wl.k)})
+    else:
+        res["note"] = "fp32 generic kernel; launch-bound at this size (parity workload)"
+    return res
+
+
+def closed_loop(elb, dev, report_every: int = 25) -> dict:
+    """The 300-step closed loop on the GPU alone: fixed router weights, fresh clustered tokens
+    every step, drawn on the GPU with the same recipe as the host generator (cluster centres and
+    Zipf weights of the workload; cluster ids from the weights, token = centre + 0.5 N(0, 1),
+    rounded to bf16 to nearest even) from torch's seeded GPU generator; one RouterStep per
+    balancer (SMEBU, sign, linear), all fed the same tokens, b and m persisting.  MaxVio (max n /
+    min n) of every step is kept on the device and read once at the end."""
+    import torch
+
+    import datagen
+
+    wl = datagen.WORKLOADS["loop"]
+    w = datagen.router_weight(wl)
+    centres, p = datagen.cluster_model(wl)
+    b0 = torch.from_numpy(datagen.initial_bias(wl)).to(dev)
+    wd = torch.from_numpy(w.view("int16")).to(dev).view(torch.bfloat16)
+    cen = torch.from_numpy(centres).to(dev)
+    pd = torch.from_numpy(p).to(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.seed)
+    steps = {m: elb.RouterStep(wd, b0.clone(), torch.zeros_like(b0), wl.k, wl.T, mode=m, lam=wl.lam, beta=wl.beta,
+                               kappa=wl.kappa, gamma=wl.gamma, dispatch=False) for m in BALANCERS}
+    mv = torch.empty((wl.steps, len(BALANCERS)), dtype=torch.float32, device=dev)
+    t0 = time.perf_counter()
+    for s in range(wl.steps):
+        c = torch.multinomial(pd, wl.T, replacement=True, generator=gen)
+        x = torch.randn((wl.T, wl.d), generator=gen, device=dev)
+        x.mul_(wl.cluster_sigma).add_(cen[c])
+        x = x.to(torch.bfloat16)
+        for j, m in enumerate(BALANCERS):
+            mv[s, j] = steps[m](x).maxvio[0]
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    h = mv.cpu().numpy()
+    marks = sorted(set(range(0, wl.steps, report_every)) | {wl.steps - 1})
+    res = {"workload": wl.label, "tokens": f"GPU-drawn (torch generator, seed {wl.seed}), host recipe",
+           "seconds": round(el, 2), "steps": wl.steps, "maxvio": "max n / min n at the listed steps"}
+    for j, m in enumerate(BALANCERS):
+        res[m] = {"at": {str(i): round(float(h[i, j]), 3) for i in marks},
+                  "mean_last_50": round(float(h[-50:, j].mean()), 3), "min": round(float(h[:, j].min()), 3),
+                  "max": round(float(h[:, j].max()), 3)}
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="large")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-next", action="store_true", help="skip the rows beside the hot path")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-loop", action="store_true", help="skip the 300-step closed loop")
     ap.add_argument("--router-launches", type=int, default=200, metavar="R",
                     help="back-to-back router launches timed for the roofline")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -263,7 +481,7 @@ def main() -> int:
         import datagen
 
         rec = summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1], int(args.summarize_traffic[2]),
-                                datagen.WORKLOADS[args.workload].T, max(1, args.router_launches))
+                                datagen.WORKLOADS[args.workload].T, max(1, args.router_launches), args.workload)
         with open(TRAFFIC_FILE, "w") as f:
             json.dump(rec, f, indent=1)
         print(json.dumps(rec))
@@ -273,7 +491,6 @@ def main() -> int:
               file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
     import datagen
@@ -283,63 +500,21 @@ def main() -> int:
     elb.lib()  # fails loudly when libelb.so is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-
-    x = datagen.tokens(wl)
-    w = datagen.router_weight(wl)
-    b0, m0 = datagen.initial_bias(wl), datagen.initial_momentum(wl)
-
-    def to_dev(a):
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
-        return torch.from_numpy(a).to(dev)
-
-    # Two copies of the tokens, alternated step by step, so no step reads its input out of the
-    # 256 MB last-level cache that the previous step filled.
-    xs = [to_dev(x), to_dev(x)]
-    wd, bd, md = to_dev(w), to_dev(b0), to_dev(m0)
-    T, d, n_e, k = wl.T, wl.d, wl.n_experts, wl.k
-    # One library call per step (elb_route_step): router kernel, dispatch scan, scatter with the
-    # bias update beside it (workloads without dispatch: router kernel, then the update).
-    # The loads accumulate into counts and the update clears them.
-    step = elb.RouterStep(wd, bd, md, k, T, mode=wl.mode, lam=wl.lam, beta=wl.beta, kappa=wl.kappa, gamma=wl.gamma,
-                          dispatch=wl.dispatch)
     stream = torch.cuda.current_stream(dev)
 
-    for i in range(args.warmup):
-        step(xs[i & 1])
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(args.steps):
-        out = step(xs[i & 1])
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    s = Setup(elb, wl, dev)
+    T, d, n_e, k = wl.T, wl.d, wl.n_experts, wl.k
+    # The timed region: exactly `steps` steps, back to back, one library call each.
+    ms, out = time_steps(s, args.steps, args.warmup, stream)
     value = T / (ms * 1e-3)
     mv = out.maxvio
+    med = step_median(s, max(50, args.steps))
 
-    # The router kernel's average launch duration, for the roofline: R launches of it back to
-    # back on the same stream (a step with neither dispatch nor update; the counts accumulate),
-    # from the end of an empty kernel launched just before the first to the end of the last.
-    # The events are fence-free and bound to those two kernels, so no marker sits between the
-    # launches; the one dispatch gap after the empty kernel is spread over the R launches.  (A
-    # marker beside every launch would add its own ~5 us dispatch gap to each.)  The clock of a
-    # power-limited part wanders over milliseconds, so R spans about as long as the steps do.
-    solo = elb.RouterStep(wd, bd, None, k, T, update=False, dispatch=False)
-    t0, t1 = TimingEvent(), TimingEvent()
     n_solo = max(1, args.router_launches)
-    for i in range(2):
-        solo(xs[i & 1])
-    torch.cuda.synchronize()
-    for i in range(n_solo):
-        solo.set_timing(t0 if i == 0 else None, t1 if i == n_solo - 1 else None)
-        solo(xs[i & 1])
-    torch.cuda.synchronize()
-    router_ms = t0.elapsed_time(t1) / n_solo
+    router_ms = router_back_to_back(elb, s, n_solo)
 
     # The dispatch (a6) through its own entry point, on the last step's indices, back to back:
-    # the counting pass, the scan and the scatter (inside the step the router kernel has done the
-    # counting).  It moves ~1% of the router's bytes and is bound by latency, not bandwidth.
+    # it moves ~1% of the router's bytes and is bound by latency, not bandwidth.
     dispatch = None
     if wl.dispatch:
         ws_d = torch.empty(elb.dispatch_workspace_bytes(T, k, n_e), dtype=torch.uint8, device=dev)
@@ -348,14 +523,11 @@ def main() -> int:
                 torch.empty(T * k, dtype=torch.int32, device=dev))
         ms_d = time_events(lambda: elb.router_dispatch(idx_last, n_e, workspace=ws_d, out=outs), 50, stream)
         alg_d = dispatch_alg_bytes(T, n_e, k)
-        dispatch = {"us": round(ms_d * 1e3, 2), "kernels": 3, "alg_bytes": alg_d,
+        dispatch = {"us": round(ms_d * 1e3, 2), "alg_bytes": alg_d,
                     "achieved_GBps": round(alg_d / (ms_d * 1e-3) / 1e9, 1),
                     "frac": round(alg_d / (ms_d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
-    alg = router_alg_bytes(T, d, n_e, k)
-    achieved = alg / (router_ms * 1e-3) / 1e9
-    flops = 2.0 * T * d * n_e
-    tflops = flops / (router_ms * 1e-3) / 1e12
+    r = roofline_of(wl, router_ms)
     traffic = traffic_from_profile(T)
     line = {
         "metric": METRIC,
@@ -372,18 +544,24 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": wl.label, "T": T, "d": d, "n_experts": n_e, "k": k, "balance": wl.mode,
                    "dispatch": wl.dispatch, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None if traffic is None else round(traffic),
-                     "kernel": router_kernel_name(T, n_e, k), "alg_bytes_per_launch": alg, "launches_timed": n_solo,
-                     "kernel_us": round(router_ms * 1e3, 2),
-                     "mfma_tflops": round(tflops, 1), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)},
-        "breakdown_us": {"step": round(ms * 1e3, 2), "router_back_to_back": round(router_ms * 1e3, 2)},
+        "roofline": {"bound": "hbm", "achieved": r["achieved"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": r["frac"], "traffic": None if traffic is None else round(traffic),
+                     "kernel": router_kernel_name(T, n_e, k), "alg_bytes_per_launch": r["alg_bytes_per_launch"],
+                     "launches_timed": n_solo, "kernel_us": r["kernel_us"], "mfma_tflops": r["mfma_tflops"],
+                     "mfma_frac": r["mfma_frac"]},
+        "breakdown_us": {"step": round(ms * 1e3, 2), "step_median": med["median"], "step_min": med["min"],
+                         "step_max": med["max"], "step_median_reps": med["reps"],
+                         "router_back_to_back": r["kernel_us"]},
         "dispatch": dispatch,
         "maxvio_last": float(mv.cpu()[0]),
     }
+    if not args.no_configs:
+        line["configs"] = {key: bench_config(elb, key, dev, stream, 50, 100) for key in OTHER_CONFIGS
+                           if key != args.workload}
+    if not args.no_loop:
+        line["closed_loop"] = closed_loop(elb, dev)
     if not args.no_next:
-        line["next_rows"] = bench_next_rows(elb, wl, xs[0], wd, out, stream)
+        line["next_rows"] = bench_next_rows(elb, wl, s.xs[0], s.wd, out, stream)
     if args.calibrate_copy:
         n = args.calibrate_copy * 1024 * 1024
         src = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -393,7 +571,7 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(wl, x, w, b0, m0)
+        line["cpu_baseline"] = cpu_baseline(wl, s.x, s.w, s.b0, s.m0)
     print(json.dumps(line), flush=True)
     return 0
 

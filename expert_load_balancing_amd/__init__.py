@@ -84,16 +84,29 @@ def router_forward(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor, k: int,
     in to be overwritten (or added to, with ``accumulate=True``); ``out`` may hold
     preallocated (topk_idx, gates) tensors.
     """
+    # Sizes first (a buffer too small would be written past its end on the device), then
+    # dtype, device and layout.
+    for t, name in ((x, "x"), (w, "w"), (bias, "bias")):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+    if x.dim() != 2 or w.dim() != 2 or bias.dim() != 1 or w.shape[1] != x.shape[1] or bias.shape[0] != w.shape[0]:
+        raise ValueError(f"shapes do not match: x {tuple(x.shape)}, w {tuple(w.shape)}, bias {tuple(bias.shape)}")
+    T, d = x.shape
+    n_e = w.shape[0]
+    if out is not None:
+        if len(out) != 2 or any(not isinstance(t, torch.Tensor) for t in out):
+            raise TypeError("out must be a (topk_idx, gates) pair of tensors")
+        if out[0].numel() != T * k or out[1].numel() != T * k:
+            raise ValueError(f"out: topk_idx and gates must hold T*k = {T * k} entries, got "
+                             f"{out[0].numel()} and {out[1].numel()}")
+    if counts is not None and (not isinstance(counts, torch.Tensor) or counts.numel() != n_e):
+        raise ValueError(f"counts must be a tensor of N_r = {n_e} entries")
     _need(x, "x")
     dev = x.device
     if x.dtype not in _DTYPES:
         raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
     _need(w, "w", x.dtype, dev)
     _need(bias, "bias", torch.float32, dev)
-    if x.dim() != 2 or w.dim() != 2 or bias.dim() != 1 or w.shape[1] != x.shape[1] or bias.shape[0] != w.shape[0]:
-        raise ValueError(f"shapes do not match: x {tuple(x.shape)}, w {tuple(w.shape)}, bias {tuple(bias.shape)}")
-    T, d = x.shape
-    n_e = w.shape[0]
     if out is None:
         idx = torch.empty((T, k), dtype=torch.int32, device=dev)
         gates = torch.empty((T, k), dtype=torch.float32, device=dev)
@@ -132,6 +145,8 @@ def router_dispatch(topk_idx: torch.Tensor, n_experts: int, *, workspace: torch.
 
     ``out``: (offsets, perm, inv or None) int32 tensors to write instead of new ones.
     """
+    if not isinstance(topk_idx, torch.Tensor) or topk_idx.dim() != 2:
+        raise ValueError("topk_idx must be a [T, k] tensor")
     _need(topk_idx, "topk_idx", torch.int32)
     dev = topk_idx.device
     T, k = topk_idx.shape
@@ -380,20 +395,20 @@ class RouterStep:
         self._args = a
         self._timing = None
 
-    def set_timing(self, start=None, stop=None) -> None:
-        """Bracket the router kernel of later calls with timing events (torch.cuda.Event or any
-        object with a ``cuda_event`` handle): ``start`` takes the end of an empty kernel launched
-        just before it, ``stop`` the router kernel's own end; either may be None, and
-        ``set_timing()`` stops it."""
-        if start is None and stop is None:
+    def set_timing(self, start=None, stop=None, end=None) -> None:
+        """Bracket the kernels of later calls with timing events (torch.cuda.Event or any object
+        with a ``cuda_event`` handle): ``start`` takes the end of an empty kernel launched just
+        before the router kernel, ``stop`` the router kernel's own end, ``end`` the end of the
+        step's last kernel; any may be None, and ``set_timing()`` stops it."""
+        if start is None and stop is None and end is None:
             self._timing, self._args.timing = None, None
             return
         handles = []
-        for ev in (start, stop):
+        for ev in (start, stop, end):
             if ev is not None and ev.cuda_event == 0:  # torch creates the HIP event on first record
                 ev.record(torch.cuda.current_stream(self.device))
             handles.append(None if ev is None else ev.cuda_event)
-        self._timing = (ctypes.c_void_p * 2)(*handles)
+        self._timing = (ctypes.c_void_p * 3)(*handles)
         self._args.timing = ctypes.cast(self._timing, ctypes.c_void_p).value
 
     def __call__(self, x: torch.Tensor) -> StepOutputs:

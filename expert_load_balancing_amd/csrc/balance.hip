@@ -58,14 +58,16 @@ __global__ __launch_bounds__(kZThreads) void zloss_kernel(const float* __restric
 
 }  // namespace
 
-hipError_t launch_balance_layers(const BalanceArgs& a, int n_layers, hipStream_t stream) {
-  return launch(balance_layers_kernel, dim3((unsigned)n_layers), dim3(64), 0, stream, a);
+hipError_t launch_balance_layers(const BalanceArgs& a, int n_layers, hipStream_t stream, hipEvent_t ev_stop) {
+  return launch_timed(balance_layers_kernel, dim3((unsigned)n_layers), dim3(64), 0, stream, nullptr, ev_stop, a);
 }
 
-hipError_t launch_balance(const BalanceArgs& a, hipStream_t stream) { return launch_balance_layers(a, 1, stream); }
+hipError_t launch_balance(const BalanceArgs& a, hipStream_t stream, hipEvent_t ev_stop) {
+  return launch_balance_layers(a, 1, stream, ev_stop);
+}
 
-hipError_t launch_zloss(const float* lse, int64_t T, float* out, hipStream_t stream) {
-  return launch(zloss_kernel, dim3(1), dim3(kZThreads), 0, stream, lse, T, out);
+hipError_t launch_zloss(const float* lse, int64_t T, float* out, hipStream_t stream, hipEvent_t ev_stop) {
+  return launch_timed(zloss_kernel, dim3(1), dim3(kZThreads), 0, stream, nullptr, ev_stop, lse, T, out);
 }
 
 }  // namespace elb

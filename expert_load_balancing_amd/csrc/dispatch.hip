@@ -172,11 +172,11 @@ __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(const int32_
 template <int K>
 hipError_t launch_scatter(const int32_t* idx, int64_t total, int n_experts, const DispatchGeom& g,
                           const int32_t* loads, const int32_t* totals, int32_t* offsets, int32_t* perm, int32_t* inv,
-                          const BalanceArgs* update, hipStream_t stream) {
+                          const BalanceArgs* update, hipStream_t stream, hipEvent_t ev_stop) {
   const BalanceArgs none{};
-  return launch(dispatch_scatter_kernel<K>, dim3((unsigned)(g.n_tiles + (update != nullptr ? 1 : 0))), dim3(kThreads),
-                0, stream, idx, total, n_experts, g.stride, loads, totals, offsets, perm, inv,
-                update != nullptr ? *update : none);
+  return launch_timed(dispatch_scatter_kernel<K>, dim3((unsigned)(g.n_tiles + (update != nullptr ? 1 : 0))),
+                      dim3(kThreads), 0, stream, nullptr, ev_stop, idx, total, n_experts, g.stride, loads, totals,
+                      offsets, perm, inv, update != nullptr ? *update : none);
 }
 
 }  // namespace
@@ -196,11 +196,12 @@ size_t dispatch_workspace_bytes(int64_t T, int n_experts) {
 
 hipError_t launch_dispatch(const int32_t* idx, int64_t T, int k, int n_experts, void* workspace, bool loads_ready,
                            const BalanceArgs* update, int32_t* offsets, int32_t* perm, int32_t* inv,
-                           hipStream_t stream) {
+                           hipStream_t stream, hipEvent_t ev_stop) {
   if (T == 0) {
     const hipError_t err = launch_fill_i32(offsets, n_experts + 1, 0, stream);
-    if (err != hipSuccess || update == nullptr) return err;
-    return launch_balance(*update, stream);
+    if (err != hipSuccess) return err;
+    if (update != nullptr) return launch_balance(*update, stream, ev_stop);
+    return ev_stop != nullptr ? launch_mark(ev_stop, stream) : hipSuccess;
   }
   const DispatchGeom g = dispatch_geometry(T);
   const int64_t total = T * k;
@@ -218,14 +219,14 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t T, int k, int n_experts, 
   const int32_t* cl = loads;
   const int32_t* ct = totals;
   switch (k) {
-    case 1: return launch_scatter<1>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, update, stream);
-    case 2: return launch_scatter<2>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, update, stream);
-    case 3: return launch_scatter<3>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, update, stream);
-    case 4: return launch_scatter<4>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, update, stream);
-    case 5: return launch_scatter<5>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, update, stream);
-    case 6: return launch_scatter<6>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, update, stream);
-    case 7: return launch_scatter<7>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, update, stream);
-    default: return launch_scatter<8>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, update, stream);
+    case 1: return launch_scatter<1>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, update, stream, ev_stop);
+    case 2: return launch_scatter<2>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, update, stream, ev_stop);
+    case 3: return launch_scatter<3>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, update, stream, ev_stop);
+    case 4: return launch_scatter<4>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, update, stream, ev_stop);
+    case 5: return launch_scatter<5>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, update, stream, ev_stop);
+    case 6: return launch_scatter<6>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, update, stream, ev_stop);
+    case 7: return launch_scatter<7>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, update, stream, ev_stop);
+    default: return launch_scatter<8>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, update, stream, ev_stop);
   }
 }
 

@@ -139,24 +139,31 @@ elb_status elb_route_step(const elb_step_args* args, elb_stream_t stream) {
   const bool mfma = !(a.flags & ELB_FORCE_GENERIC) && elb::router_mfma_applies(ra);
   const bool loads_ready = dispatch && mfma && elb::router_mfma_full_tile(a.T);  // the router fills the table
   if (!loads_ready) ra.tile_loads = nullptr;
+  hipEvent_t ev_end = nullptr;  // the end of the step's last kernel
   if (a.timing != nullptr) {
     // From the end of an empty kernel launched just before the router kernel to its end.
     if (a.timing[0] != nullptr && elb::launch_mark(static_cast<hipEvent_t>(a.timing[0]), s) != hipSuccess)
       return ELB_ERR_LAUNCH;
     ra.ev_stop = static_cast<hipEvent_t>(a.timing[1]);
+    ev_end = static_cast<hipEvent_t>(a.timing[2]);
   }
+  const bool router_last = a.zloss == nullptr && !dispatch && a.update == 0;
   if (a.T > 0) {
     const hipError_t err = mfma ? elb::launch_router_mfma(ra, s) : elb::launch_router_generic(ra, s);
     if (err != hipSuccess) return ELB_ERR_LAUNCH;
   } else if (ra.ev_stop != nullptr && elb::launch_mark(ra.ev_stop, s) != hipSuccess) {  // no router kernel
     return ELB_ERR_LAUNCH;
   }
-  if (a.zloss != nullptr && elb::launch_zloss(a.lse, a.T, a.zloss, s) != hipSuccess) return ELB_ERR_LAUNCH;
+  // A step of the router kernel alone: the end event follows it on an empty kernel.
+  if (router_last) return ev_end != nullptr ? from_hip(elb::launch_mark(ev_end, s)) : ELB_OK;
+  if (a.zloss != nullptr &&
+      elb::launch_zloss(a.lse, a.T, a.zloss, s, (!dispatch && a.update == 0) ? ev_end : nullptr) != hipSuccess)
+    return ELB_ERR_LAUNCH;
   const elb::BalanceArgs upd =
       balance_args(a.counts, a.n_experts, a.params, a.bias, a.momentum, a.delta_b, a.maxvio);
-  if (!dispatch) return a.update != 0 ? from_hip(elb::launch_balance(upd, s)) : ELB_OK;
+  if (!dispatch) return a.update != 0 ? from_hip(elb::launch_balance(upd, s, ev_end)) : ELB_OK;
   return from_hip(elb::launch_dispatch(a.topk_idx, a.T, a.k, a.n_experts, a.workspace, loads_ready,
-                                       a.update != 0 ? &upd : nullptr, a.offsets, a.perm, a.inv_perm, s));
+                                       a.update != 0 ? &upd : nullptr, a.offsets, a.perm, a.inv_perm, s, ev_end));
 }
 
 elb_status elb_smebu_update_layers(int32_t* counts, int32_t n_layers, int32_t n_experts, elb_balance_params params,

@@ -91,14 +91,17 @@ DispatchGeom dispatch_geometry(int64_t T);
 size_t dispatch_workspace_bytes(int64_t T, int n_experts);
 // loads_ready: the router kernel already filled the loads table for this batch.
 // update: NULL, or a bias update to run beside the scatter (one extra workgroup).
+// ev_stop: NULL, or an event that takes the end time stamp of the dispatch's last kernel.
 hipError_t launch_dispatch(const int32_t* idx, int64_t T, int k, int n_experts, void* workspace, bool loads_ready,
                            const BalanceArgs* update, int32_t* offsets, int32_t* perm, int32_t* inv,
-                           hipStream_t stream);
+                           hipStream_t stream, hipEvent_t ev_stop = nullptr);
 
-hipError_t launch_balance(const BalanceArgs& a, hipStream_t stream);
+// ev_stop (optional): an event that takes the kernel's end time stamp.
+hipError_t launch_balance(const BalanceArgs& a, hipStream_t stream, hipEvent_t ev_stop = nullptr);
 // n_layers independent updates, layer l at offset l * a.n (maxvio at 2 l).
-hipError_t launch_balance_layers(const BalanceArgs& a, int n_layers, hipStream_t stream);
-hipError_t launch_zloss(const float* lse, int64_t T, float* out, hipStream_t stream);
+hipError_t launch_balance_layers(const BalanceArgs& a, int n_layers, hipStream_t stream,
+                                 hipEvent_t ev_stop = nullptr);
+hipError_t launch_zloss(const float* lse, int64_t T, float* out, hipStream_t stream, hipEvent_t ev_stop = nullptr);
 
 // router_backward.hip (bf16, d % 64 == 0).
 struct BackwardArgs {

@@ -12,8 +12,10 @@
 //    tokens cost T * row_bytes of reads instead of K * T (a gather by expert row would re-read
 //    every token K times, from HBM, since its K copies are far apart in the buffer);
 //  * combine gathers by token: one wave per token reads its K expert rows and writes y once;
-//  * one wave owns one token row; its lanes move 16 bytes each per step, rows are walked in
-//    steps of 1 KiB with several steps in flight;
+//  * one wave owns one token row at a time; its lanes move 16 bytes each per step, rows are
+//    walked in steps of 1 KiB with several steps in flight.  The grid is capped (kMaxBlocks)
+//    and the waves stride over the tokens, so every T the API accepts launches (a grid of one
+//    wave per token would pass the 32-bit work-item count of a dispatch at T = 2^26);
 //  * everything is read or written exactly once, so all global traffic is non-temporal.
 #include "../../include/elb.h"
 #include "device_common.hpp"
@@ -27,6 +29,7 @@ using f32x4 = float __attribute__((ext_vector_type(4)));
 
 constexpr int kWavesPerBlock = 4;
 constexpr int kUnrollRow = 4;  // 16-byte chunks in flight per lane
+constexpr int64_t kMaxBlocks = int64_t(1) << 20;  // 4 Mi waves, far more than the GPU holds at once
 
 __device__ __forceinline__ u32x4 load_nt(const u32x4* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void store_nt(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
@@ -37,26 +40,27 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void permute_rows_kernel(const
                                                                            const int32_t* __restrict__ inv,
                                                                            u32x4* __restrict__ xp) {
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (t >= T) return;
-  int64_t dst[8];
+  for (int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6); t < T;
+       t += (int64_t)gridDim.x * kWavesPerBlock) {
+    int64_t dst[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) dst[j] = j < k ? (int64_t)inv[t * k + j] * chunks : 0;
-  const u32x4* src = x + t * chunks;
-  for (int64_t c0 = 0; c0 < chunks; c0 += 64 * kUnrollRow) {
-    u32x4 v[kUnrollRow];
+    for (int j = 0; j < 8; ++j) dst[j] = j < k ? (int64_t)inv[t * k + j] * chunks : 0;
+    const u32x4* src = x + t * chunks;
+    for (int64_t c0 = 0; c0 < chunks; c0 += 64 * kUnrollRow) {
+      u32x4 v[kUnrollRow];
 #pragma unroll
-    for (int u = 0; u < kUnrollRow; ++u) {
-      const int64_t c = c0 + u * 64 + lane;
-      if (c < chunks) v[u] = load_nt(src + c);
-    }
+      for (int u = 0; u < kUnrollRow; ++u) {
+        const int64_t c = c0 + u * 64 + lane;
+        if (c < chunks) v[u] = load_nt(src + c);
+      }
 #pragma unroll
-    for (int u = 0; u < kUnrollRow; ++u) {
-      const int64_t c = c0 + u * 64 + lane;
-      if (c < chunks) {
+      for (int u = 0; u < kUnrollRow; ++u) {
+        const int64_t c = c0 + u * 64 + lane;
+        if (c < chunks) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (j < k) store_nt(xp + dst[j] + c, v[u]);
+          for (int j = 0; j < 8; ++j)
+            if (j < k) store_nt(xp + dst[j] + c, v[u]);
+        }
       }
     }
   }
@@ -85,76 +89,80 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void combine_kernel(const u32x
                                                                       const float* __restrict__ gates,
                                                                       void* __restrict__ y) {
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (t >= T) return;
-  constexpr int kPer = IN_BF16 ? 8 : 4;  // elements per chunk
-  int64_t src[8];
-  float g[8];
+  for (int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6); t < T;
+       t += (int64_t)gridDim.x * kWavesPerBlock) {
+    constexpr int kPer = IN_BF16 ? 8 : 4;  // elements per chunk
+    int64_t src[8];
+    float g[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    src[j] = j < k ? (int64_t)inv[t * k + j] * chunks : 0;
-    g[j] = j < k ? gates[t * k + j] : 0.0f;
-  }
-  for (int64_t c0 = 0; c0 < chunks; c0 += 64 * 2) {
-    float acc[2][kPer];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int e = 0; e < kPer; ++e) acc[u][e] = 0.0f;
-    u32x4 v[2][8];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int64_t c = c0 + u * 64 + lane;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (j < k && c < chunks) v[u][j] = load_nt(eo + src[j] + c);
+    for (int j = 0; j < 8; ++j) {
+      src[j] = j < k ? (int64_t)inv[t * k + j] * chunks : 0;
+      g[j] = j < k ? gates[t * k + j] : 0.0f;
     }
+    for (int64_t c0 = 0; c0 < chunks; c0 += 64 * 2) {
+      float acc[2][kPer];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int64_t c = c0 + u * 64 + lane;
-      if (c >= chunks) continue;
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (j >= k) break;
-        float f[kPer];
-        if constexpr (IN_BF16) {
-          widen8(v[u][j], f);
-        } else {
+        for (int e = 0; e < kPer; ++e) acc[u][e] = 0.0f;
+      u32x4 v[2][8];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(v[u][j][e]);
-        }
+      for (int u = 0; u < 2; ++u) {
+        const int64_t c = c0 + u * 64 + lane;
 #pragma unroll
-        for (int e = 0; e < kPer; ++e) acc[u][e] = __builtin_fmaf(g[j], f[e], acc[u][e]);
+        for (int j = 0; j < 8; ++j)
+          if (j < k && c < chunks) v[u][j] = load_nt(eo + src[j] + c);
       }
-      const int64_t e0 = c * kPer;  // first element of this chunk in the row
-      if constexpr (OUT_BF16) {
-        uint32_t* yo = static_cast<uint32_t*>(y) + (t * chunks * kPer + e0) / 2;
-        if constexpr (kPer == 8) {
-          u32x4 o;
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            o[q] = f32_to_bf16_rne(acc[u][2 * q]) | (f32_to_bf16_rne(acc[u][2 * q + 1]) << 16);
-          store_nt(reinterpret_cast<u32x4*>(yo), o);
-        } else {
-          using u32x2 = unsigned int __attribute__((ext_vector_type(2)));
-          u32x2 o;
-          o[0] = f32_to_bf16_rne(acc[u][0]) | (f32_to_bf16_rne(acc[u][1]) << 16);
-          o[1] = f32_to_bf16_rne(acc[u][2]) | (f32_to_bf16_rne(acc[u][3]) << 16);
-          __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(yo));
+      for (int u = 0; u < 2; ++u) {
+        const int64_t c = c0 + u * 64 + lane;
+        if (c >= chunks) continue;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (j >= k) break;
+          float f[kPer];
+          if constexpr (IN_BF16) {
+            widen8(v[u][j], f);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(v[u][j][e]);
+          }
+#pragma unroll
+          for (int e = 0; e < kPer; ++e) acc[u][e] = __builtin_fmaf(g[j], f[e], acc[u][e]);
         }
-      } else {
-        float* yo = static_cast<float*>(y) + t * chunks * kPer + e0;
+        const int64_t e0 = c * kPer;  // first element of this chunk in the row
+        if constexpr (OUT_BF16) {
+          uint32_t* yo = static_cast<uint32_t*>(y) + (t * chunks * kPer + e0) / 2;
+          if constexpr (kPer == 8) {
+            u32x4 o;
 #pragma unroll
-        for (int q = 0; q < kPer / 4; ++q) {
-          const f32x4 o{acc[u][4 * q], acc[u][4 * q + 1], acc[u][4 * q + 2], acc[u][4 * q + 3]};
-          __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(yo) + q);
+            for (int q = 0; q < 4; ++q)
+              o[q] = f32_to_bf16_rne(acc[u][2 * q]) | (f32_to_bf16_rne(acc[u][2 * q + 1]) << 16);
+            store_nt(reinterpret_cast<u32x4*>(yo), o);
+          } else {
+            using u32x2 = unsigned int __attribute__((ext_vector_type(2)));
+            u32x2 o;
+            o[0] = f32_to_bf16_rne(acc[u][0]) | (f32_to_bf16_rne(acc[u][1]) << 16);
+            o[1] = f32_to_bf16_rne(acc[u][2]) | (f32_to_bf16_rne(acc[u][3]) << 16);
+            __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(yo));
+          }
+        } else {
+          float* yo = static_cast<float*>(y) + t * chunks * kPer + e0;
+#pragma unroll
+          for (int q = 0; q < kPer / 4; ++q) {
+            const f32x4 o{acc[u][4 * q], acc[u][4 * q + 1], acc[u][4 * q + 2], acc[u][4 * q + 3]};
+            __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(yo) + q);
+          }
         }
       }
     }
   }
 }
 
-dim3 token_grid(int64_t T) { return dim3((unsigned)((T + kWavesPerBlock - 1) / kWavesPerBlock)); }
+dim3 token_grid(int64_t T) {
+  const int64_t blocks = (T + kWavesPerBlock - 1) / kWavesPerBlock;
+  return dim3((unsigned)(blocks < kMaxBlocks ? blocks : kMaxBlocks));
+}
 
 }  // namespace
 

@@ -28,14 +28,18 @@
 //   non-temporal): d is consumed in stages of 64 elements through a DMA ring in LDS.
 //
 // Epilogue (per lane, per token): s = 1 / (1 + 2^(-z log2 e)) with the hardware exp2/rcp;
-//   the selection key is the fp32 bit pattern of s + b' with its low 8 bits replaced by an
-//   index, where b' = b + (1 - min b) >= 1 keeps every key a positive float, so float max and
-//   med3 order keys exactly like (s + b, -index).  Inside a lane the index is the lane-local
-//   slot (ascending with the expert id); the K survivors are re-keyed with 255 - expert before
-//   the cross-lane merge.  Keeping 24 bits of s + b' resolves differences down to
-//   2^-15 (1 + max b - min b); closer calls go to the lower index.  Insertion into a sorted
-//   top-K list is one max plus K-1 med3.  The chosen experts' exact scores come back through
-//   LDS for the gates.  Loads: LDS histogram, one global atomic per expert per workgroup.
+//   the selection key is an unsigned integer: a fixed-point code of v = s + b - min b in its
+//   high 23 bits and an index in its low 8 bits, so integer max and med3 order keys exactly
+//   like (s + b, -index).  The code is formed with one fma: with 2^E <= 1 + max b - min b <
+//   2^(E+1) and scale = 2^(22-E), fl(s * scale + (b - min b) * scale + 2^23 + 1) lies in
+//   [2^23, 2^24], where a float's mantissa bits are the integer itself; shifting the bit
+//   pattern left by 8 drops the exponent and leaves the code, >= 1 (the code of an absent
+//   expert is 0).  Codes resolve s + b to 2^(E-22): 2.4e-7 for a bias spread below 1,
+//   under 1e-3 for any spread below 8191; closer calls go to the lower index.  Inside a lane
+//   the index is the lane-local slot (ascending with the expert id); the K survivors are
+//   re-keyed with 255 - expert before the cross-lane merge.  Insertion into a sorted top-K
+//   list is one max plus K-1 med3.  The chosen experts' exact scores come back through LDS
+//   for the gates.  Loads: LDS histogram, one global atomic per expert per workgroup.
 #include "device_common.hpp"
 #include "elb_kernels.h"
 #include "mfma_tile.hpp"
@@ -52,12 +56,36 @@ constexpr int kTile = kRowsB;             // tokens per workgroup of the full ti
 constexpr int kCus = 256;                 // compute units of the MI355X
 constexpr float kLog2e = 1.4426950408889634f;
 
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return __builtin_elementwise_max(a, b); }
+// Median of three (one v_med3_u32).
+__device__ __forceinline__ uint32_t umed3(uint32_t a, uint32_t b, uint32_t c) {
+  return umax(__builtin_elementwise_min(a, b), __builtin_elementwise_min(umax(a, b), c));
+}
+
 // Sorted (descending) top-K insertion: the new j-th largest is med3(old (j-1)-th, old j-th, x).
 template <int K>
-__device__ __forceinline__ void topk_insert(float (&top)[K], float x) {
+__device__ __forceinline__ void topk_insert(uint32_t (&top)[K], uint32_t x) {
 #pragma unroll
-  for (int j = K - 1; j > 0; --j) top[j] = __builtin_amdgcn_fmed3f(top[j - 1], top[j], x);
-  top[0] = fmaxf(top[0], x);
+  for (int j = K - 1; j > 0; --j) top[j] = umed3(top[j - 1], top[j], x);
+  top[0] = umax(top[0], x);
+}
+
+// Selection scaling from the bias range (identical in every workgroup: min and max are exact).
+// With 2^E <= 1 + (max b - min b) < 2^(E+1): scale = 2^(22-E), so that s * scale + (b - min b) *
+// scale < 2^23 + 1 for every s in [0, 1].
+__device__ __forceinline__ float key_scale(float bmin, float bmax) {
+  const int E = (int)((__float_as_uint(1.0f + (bmax - bmin)) >> 23) & 0xFF) - 127;
+  return __uint_as_float((uint32_t)(127 + 22 - E) << 23);
+}
+
+// Per-expert addend of the key fma: (b - min b) * scale + 2^23 + 1.
+__device__ __forceinline__ float key_bias(float b, float bmin, float scale) {
+  return (b - bmin) * scale + 8388609.0f;
+}
+
+// Key of score s (fixed-point code of s + b - min b, see the file header) with index bits id.
+__device__ __forceinline__ uint32_t sel_key(float s, float scale, float kb, uint32_t id) {
+  return (__float_as_uint(__builtin_fmaf(s, scale, kb)) << 8) | id;
 }
 
 __device__ __forceinline__ float sigmoid_fast(float z) {
@@ -70,11 +98,11 @@ __device__ __forceinline__ float sigmoid_fast(float z) {
 // lane-local slot in the low bits, re-keyed with 255 - expert before the merges), parks its
 // scores, and leaves its K keys (and, with EXTRA, its log-sum-exp partial) in LDS; after a
 // barrier one wave of each pair (eh = block parity) merges the partner's K keys and writes the
-// token's indices, gates and histogram counts.  b' (the shifted bias) is in ws1[0..1 KiB), the
-// histogram in ws1[1..2 KiB).
+// token's indices, gates and histogram counts.  The key addends (key_bias) are in ws1[0..1 KiB),
+// the histogram in ws1[1..2 KiB).
 template <int K, bool FULL, bool EXTRA, int NB>
 __device__ __forceinline__ void epilogue_split(const f32x16 (&acc)[kMB / 2][NB], int tid, int wave, int lane,
-                                               int64_t row0, int64_t T, int n_experts, int normalize, float bshift,
+                                               int64_t row0, int64_t T, int n_experts, int normalize, float kbias, float kscale,
                                                unsigned char* xs0, unsigned char* xs1, unsigned char* xs2,
                                                unsigned char* ws0, unsigned char* ws1, int32_t* __restrict__ idx_out,
                                                float* __restrict__ gates_out, float* __restrict__ logits,
@@ -83,12 +111,12 @@ __device__ __forceinline__ void epilogue_split(const f32x16 (&acc)[kMB / 2][NB],
   const int h = lane >> 5;
   const int l32 = lane & 31;
   const int eh = wave & 1, tq = wave >> 1;
-  float* const bprime = reinterpret_cast<float*>(ws1);
+  float* const kb_lds = reinterpret_cast<float*>(ws1);
   int* const hist = reinterpret_cast<int*>(ws1 + 1024);
-  float* const xkey = reinterpret_cast<float*>(ws1 + 2048);                   // [8 waves][32 tokens][8]
+  uint32_t* const xkey = reinterpret_cast<uint32_t*>(ws1 + 2048);             // [8 waves][32 tokens][8]
   float2* const xlse = reinterpret_cast<float2*>(ws1 + 2048 + 8 * 32 * 8 * 4);  // [8 waves][32 tokens]
   if (tid < kExp) {
-    bprime[tid] = tid < n_experts ? bshift : 0.0f;
+    kb_lds[tid] = tid < n_experts ? kbias : 0.0f;
     hist[tid] = 0;
   }
   // Parks: wave v's scores in the 16 KiB half (v & 1) of slot v / 2, [16 groups][64 lanes][4].
@@ -102,23 +130,23 @@ __device__ __forceinline__ void epilogue_split(const f32x16 (&acc)[kMB / 2][NB],
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int64_t t = row0 + tq * (32 * NB) + nb * 32 + l32;
-    float top[K];
+    uint32_t top[K];
 #pragma unroll
-    for (int j = 0; j < K; ++j) top[j] = 0.0f;
+    for (int j = 0; j < K; ++j) top[j] = 0u;
 #pragma unroll
     for (int mb = 0; mb < kMBw; ++mb) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int e0 = 128 * eh + mb * 32 + g * 8 + 4 * h;
-        const f32x4 bp = *reinterpret_cast<const f32x4*>(bprime + e0);
+        const f32x4 kb = *reinterpret_cast<const f32x4*>(kb_lds + e0);
         f32x4 sv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float sc = sigmoid_fast(acc[mb][nb][g * 4 + r]);
           sv[r] = sc;
           const uint32_t slot_id = (uint32_t)(63 - (mb * 16 + g * 4 + r));  // lane-local, ascending expert
-          const float key = __uint_as_float((__float_as_uint(sc + bp[r]) & 0xFFFFFF00u) | slot_id);
-          topk_insert<K>(top, FULL || e0 + r < n_experts ? key : 0.0f);
+          const uint32_t key = sel_key(sc, kscale, kb[r], slot_id);
+          topk_insert<K>(top, FULL || e0 + r < n_experts ? key : 0u);
         }
         *reinterpret_cast<f32x4*>(park + ((mb * 4 + g) * 64 + lane) * 4) = sv;
       }
@@ -126,12 +154,12 @@ __device__ __forceinline__ void epilogue_split(const f32x16 (&acc)[kMB / 2][NB],
     // Re-key with the global expert id, merge with lane ^ 32 (the wave's other 64 experts).
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-      const uint32_t bits = __float_as_uint(top[j]);
+      const uint32_t bits = top[j];
       const int ls = 63 - (int)(bits & 0x3Fu);
       const int e = 128 * eh + (((ls >> 2) << 3) | (h << 2) | (ls & 3));
-      top[j] = __uint_as_float((bits & 0xFFFFFF00u) | (uint32_t)(255 - e));
+      top[j] = (bits & 0xFFFFFF00u) | (uint32_t)(255 - e);
     }
-    float other[K];
+    uint32_t other[K];
 #pragma unroll
     for (int j = 0; j < K; ++j) other[j] = __shfl_xor(top[j], 32);
 #pragma unroll
@@ -189,7 +217,7 @@ __device__ __forceinline__ void epilogue_split(const f32x16 (&acc)[kMB / 2][NB],
         float ssum = 0.0f;
 #pragma unroll
         for (int j = 0; j < K; ++j) {
-          e[j] = 255 - (int)(__float_as_uint(top[j]) & 0xFFu);
+          e[j] = 255 - (int)(top[j] & 0xFFu);
           const int el = e[j] & 127;
           const float* const pk = park_of(2 * tq + (e[j] >> 7));
           sg[j] = pk[(((el >> 5) * 4 + ((el & 31) >> 3)) * 64 + l32 + 32 * ((el >> 2) & 1)) * 4 + (el & 3)];
@@ -249,10 +277,10 @@ __global__ __launch_bounds__(TG * 128) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int rows = (int)(T - row0 < kTok ? T - row0 : kTok);
 
   // Bias loads go first: a load issued behind the DMA prologue would have to wait for it.
-  // Each wave reads all of b (4 values per lane) to form min b without any LDS.
+  // Each wave reads all of b (4 values per lane) to form min b and max b without any LDS.
   float bq[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) bq[c] = lane + 64 * c < n_experts ? bias[lane + 64 * c] : __builtin_inff();
+  for (int c = 0; c < 4; ++c) bq[c] = lane + 64 * c < n_experts ? bias[lane + 64 * c] : __builtin_nanf("");
 
   // ---- operand streams: start the DMA ring (A = weights, B = this tile's tokens) ----
   const uint32_t row_bytes = (uint32_t)d * 2u;
@@ -261,17 +289,21 @@ __global__ __launch_bounds__(TG * 128) __attribute__((amdgpu_waves_per_eu(2, 2))
           d / kBK, wave, lane, Slots{xs0, xs1, xs2, ws0, ws1});
   st.prologue();
 
-  // ---- shifted bias b' = b + (1 - min b) >= 1, so every selection key is a positive float ----
+  // ---- selection key scaling from min b and max b (fminf / fmaxf skip the NaN padding) ----
   float mn = fminf(fminf(bq[0], bq[1]), fminf(bq[2], bq[3]));
+  float mx = fmaxf(fmaxf(bq[0], bq[1]), fmaxf(bq[2], bq[3]));
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) mn = fminf(mn, __shfl_xor(mn, off));
-  const float shift = 1.0f - mn;  // identical in every wave: min is exact
-  const float bv = tid < n_experts ? bias[tid] : 0.0f;
+  for (int off = 32; off > 0; off >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, off));
+    mx = fmaxf(mx, __shfl_xor(mx, off));
+  }
+  const float kscale = key_scale(mn, mx);  // identical in every wave: min and max are exact
+  const float kbias = tid < n_experts ? key_bias(bias[tid], mn, kscale) : 0.0f;
 
   f32x16 acc[kMB / 2][NB];
   st.run(acc, wave, lane);
-  epilogue_split<K, FULL, EXTRA, NB>(acc, tid, wave, lane, row0, T, n_experts, normalize, bv + shift, xs0, xs1, xs2,
-                                     ws0, ws1, idx_out, gates_out, logits, lse);
+  epilogue_split<K, FULL, EXTRA, NB>(acc, tid, wave, lane, row0, T, n_experts, normalize, kbias, kscale, xs0, xs1,
+                                     xs2, ws0, ws1, idx_out, gates_out, logits, lse);
 
   int* const hist = reinterpret_cast<int*>(ws1 + 1024);
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);

@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define ELB_VERSION 10500 /* major * 10000 + minor * 100 + patch */
+#define ELB_VERSION 10600 /* major * 10000 + minor * 100 + patch */
 
 typedef struct ihipStream_t* elb_stream_t; /* hipStream_t; NULL = default stream */
 
@@ -104,10 +104,12 @@ typedef struct {
  * Supported: 0 <= T, T * k < 2^31; 1 <= k <= min(8, n_experts); n_experts <= 256;
  * d >= 1 with every row 16-byte aligned (d % 8 == 0 for bf16, d % 4 == 0 for fp32);
  * x and w 16-byte aligned.  bf16 inputs with d % 64 == 0 run on the MFMA kernel, which ranks
- * s + b by keys that resolve differences down to 2^-15 (1 + max b - min b) (about 3e-5 for the
- * biases SMEBU produces; closer candidates go to the lower expert index); the generic kernel
- * (ELB_FORCE_GENERIC) compares s + b exactly in fp32.  Inputs must be finite.  Errors: ELB_ERR_NULL, ELB_ERR_SHAPE, ELB_ERR_ALIGN,
- * ELB_ERR_UNSUPPORTED (dtype or flag), ELB_ERR_LAUNCH.
+ * s + b by 23-bit fixed-point codes of s + b - min b: differences resolve down to 2^(E-22),
+ * where 2^E <= 1 + max b - min b < 2^(E+1) (2.4e-7 for any bias spread below 1, finer than
+ * 1e-3 for any spread below 8191; closer candidates go to the lower expert index); the
+ * generic kernel (ELB_FORCE_GENERIC) compares s + b exactly in fp32.  Inputs must be finite.
+ * Errors: ELB_ERR_NULL, ELB_ERR_SHAPE, ELB_ERR_ALIGN, ELB_ERR_UNSUPPORTED (dtype or flag),
+ * ELB_ERR_LAUNCH.
  */
 elb_status elb_router_forward(const void* x, int32_t dtype, int64_t T, int32_t d, const void* w,
                               const float* bias, int32_t n_experts, int32_t k, uint32_t flags,
@@ -173,12 +175,13 @@ elb_status elb_smebu_update(int32_t* counts, int32_t n_experts, elb_balance_para
  * The MFMA router takes 128-token tiles for batches of at most 128 x 256 tokens and 64-token
  * tiles for at most 64 x 256 (so that every compute unit gets a tile); the dispatch then counts
  * the loads itself.
- * timing: NULL, or two hipEvent_t (either may be NULL) that bracket the router kernel: the
- * first takes the end time stamp of an empty one-wave kernel launched right before it, the
- * second the router kernel's own end (both through hipExtLaunchKernel; with T == 0 the empty
- * kernel stands in for the router kernel).  Events created with hipEventDisableSystemFence are
- * bound to the kernels' time stamps; with other events the runtime records markers after the
- * kernels, which adds their cost to the interval.  Either way the next kernel starts a few
+ * timing: NULL, or an array of three hipEvent_t (any may be NULL): [0] takes the end time
+ * stamp of an empty one-wave kernel launched right before the router kernel, [1] the router
+ * kernel's own end, [2] the end of the step's last kernel (all through hipExtLaunchKernel; with
+ * T == 0 an empty kernel stands in for the router kernel, and when the router kernel is the
+ * step's only kernel [2] goes to an empty kernel after it).  Events created with
+ * hipEventDisableSystemFence are bound to the kernels' time stamps; with other events the
+ * runtime records markers after the kernels, which adds their cost to the interval.  Either way the next kernel starts a few
  * microseconds later than it would without the event.  A measuring aid.
  */
 typedef struct {

@@ -269,3 +269,30 @@ def test_router_backward_rejects(lib, kw, want):
     st = lib.elb_router_backward(a["x"], a["dtype"], a["T"], a["d"], a["w"], a["n"], a["k"], a["flags"], a["idx"],
                                  a["g"], a["zc"], a["dx"], a["dw"], a["ws"], a["ws_bytes"], None)
     assert st == want
+
+
+def test_binding_checks_buffer_sizes_before_the_device():
+    """The Python binding refuses caller buffers of the wrong size before anything else (a
+    buffer too small would be written past its end on the device); these checks need no GPU."""
+    import torch
+
+    import expert_load_balancing_amd as elb
+
+    x = torch.zeros(10, 64, dtype=torch.bfloat16)
+    w = torch.zeros(256, 64, dtype=torch.bfloat16)
+    b = torch.zeros(256)
+    i32 = torch.int32
+    with pytest.raises(ValueError, match="T\\*k = 40"):
+        elb.router_forward(x, w, b, 4, out=(torch.zeros(10, 3, dtype=i32), torch.zeros(10, 4)))
+    with pytest.raises(ValueError, match="T\\*k = 40"):
+        elb.router_forward(x, w, b, 4, out=(torch.zeros(10, 4, dtype=i32), torch.zeros(39)))
+    with pytest.raises(ValueError, match="N_r = 256"):
+        elb.router_forward(x, w, b, 4, counts=torch.zeros(255, dtype=i32))
+    with pytest.raises(ValueError, match="shapes do not match"):
+        elb.router_forward(x, w[:, :32], b, 4)
+    with pytest.raises(ValueError, match=r"\[T, k\]"):
+        elb.router_dispatch(torch.zeros(40, dtype=i32), 256)
+    # Right sizes: the next refusal is the device.
+    with pytest.raises(ValueError, match="GPU"):
+        elb.router_forward(x, w, b, 4, out=(torch.zeros(10, 4, dtype=i32), torch.zeros(10, 4)),
+                           counts=torch.zeros(256, dtype=i32))

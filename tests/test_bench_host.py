@@ -102,10 +102,44 @@ def test_traffic_record_applies_only_to_its_source_and_size(tmp_path, monkeypatc
 
 def test_committed_traffic_record_is_near_the_algorithmic_bytes():
     """The record in profiles/ (when taken on the current router source): counted HBM bytes of a
-    launch of the large workload within 10% above its algorithmic bytes."""
+    launch of its workload within 10% above its algorithmic bytes."""
+    import datagen
+
     with open(bench.TRAFFIC_FILE) as f:
         rec = json.load(f)
     if rec["kernel_source_sha256"] != bench.kernel_source_hash():
         pytest.skip("the traffic record predates the router source (the bench reports traffic null)")
-    alg = bench.router_alg_bytes(rec["T"], 3072, 256, 4)
+    wl = datagen.WORKLOADS[rec.get("workload", "large")]
+    assert wl.T == rec["T"]
+    alg = bench.router_alg_bytes(wl.T, wl.d, wl.n_experts, wl.k)
     assert 1.0 <= rec["traffic_bytes_per_launch"] / alg < 1.1
+
+
+def test_stress_workload_is_the_default_and_its_bytes():
+    """The headline is the largest single-GPU workload: T = 262144, d = 4096 (2.158 GB per launch)."""
+    import datagen
+
+    wl = datagen.WORKLOADS[bench.DEFAULT_WORKLOAD]
+    assert (wl.T, wl.d, wl.n_experts, wl.k) == (262144, 4096, 256, 4)
+    assert bench.router_alg_bytes(wl.T, wl.d, wl.n_experts, wl.k) == 2_157_971_456
+
+
+def test_oracle_threads_follow_the_affinity_mask_and_the_host_share(monkeypatch):
+    aff = len(os.sched_getaffinity(0))
+    monkeypatch.delenv("OMP_NUM_THREADS", raising=False)
+    assert bench.oracle_threads() == (aff, aff)
+    monkeypatch.setenv("OMP_NUM_THREADS", "1")
+    assert bench.oracle_threads() == (1, aff)
+    monkeypatch.setenv("OMP_NUM_THREADS", str(aff + 100))
+    assert bench.oracle_threads() == (aff, aff)
+
+
+def test_cpu_baseline_reports_cores_and_single_thread_samples():
+    """The CPU leg on a small workload: all cores of the affinity mask, then one-thread samples."""
+    import datagen
+
+    wl = datagen.WORKLOADS["tiny"]
+    res = bench.cpu_baseline(wl, datagen.tokens(wl), datagen.router_weight(wl), datagen.initial_bias(wl),
+                             datagen.initial_momentum(wl), min_seconds=0.2, max_seconds=1.0, single_thread=False)
+    assert res["kind"] == "oracle" and res["value"] > 0
+    assert res["cores"] == bench.oracle_threads()[0] and res["affinity_cores"] == len(os.sched_getaffinity(0))

@@ -2,9 +2,11 @@
 step; b and m persist on the GPU.  The same token stream drives three balancers side by side
 (SMEBU, the Nano/Mini sign step and the linear unclamped step).
 
-Every step is teacher-forced: the oracle routes a sample of that step's tokens with the
-GPU's own pre-step bias, counts the GPU's indices, and applies its update to the GPU's
-counts and pre-step b, m; b and m must agree within 1e-6.  (A free-running oracle would
+Every step is teacher-forced: the oracle routes that step's tokens with the GPU's own
+pre-step bias (every token at steps 0, 25, 50, ... and the last step, for all three modes; a
+seeded sample plus the ragged tail otherwise), counts the GPU's indices, and applies its
+update to the GPU's counts and pre-step b, m; b and m must agree within 1e-6.  Near-ties of the
+whole-batch checks are counted and reported per mode.  (A free-running oracle would
 drift by design: one excused near-tie moves a load by one, which moves the step by about
 lambda kappa / nbar.)  A resume check restarts SMEBU from a copy of (b, m) taken 50 steps
 before the end and must land on the same bits."""
@@ -32,12 +34,14 @@ def test_closed_loop_three_balancers():
     maxvio = {m: [] for m in MODES}
     worst = {m: 0.0 for m in MODES}
     ties = 0
+    full = {m: None for m in MODES}  # merged whole-batch checks per mode
     resume_at = wl.steps - 50
     saved = None
     for step in range(wl.steps):
         x = datagen.tokens(wl, step=step)
         xd = to_dev(x)
-        rows = sample_rows(wl.T, 48, seed=step)
+        whole = step % 25 == 0 or step == wl.steps - 1
+        rows = None if whole else sample_rows(wl.T, 48, seed=step)
         for mode in MODES:
             bd, md = state[mode]
             b_prev, m_prev = bd.cpu().numpy(), md.cpu().numpy()
@@ -50,6 +54,9 @@ def test_closed_loop_three_balancers():
             idx_h, counts_h = idx.cpu().numpy(), counts.cpu().numpy()
             rep = compare_route(idx_h, gates.cpu().numpy(), x, w, b_prev, wl.k, rows)
             ties += rep.ties
+            if whole:
+                assert rep.n_tokens == wl.T
+                full[mode] = rep if full[mode] is None else full[mode].merge(rep)
             c64 = check_counts(counts_h, idx_h, wl.n_experts)
             worst[mode] = max(worst[mode], check_balance(mode, c64, b_prev, m_prev, bd.cpu().numpy(),
                                                          md.cpu().numpy(), wl))
@@ -59,7 +66,9 @@ def test_closed_loop_three_balancers():
     for m in MODES:
         log(f"{m}: max |b,m error| {worst[m]:.2e}; MaxVio first {maxvio[m][0]:.2f} "
             f"mean of last 50 {np.mean(maxvio[m][-50:]):.2f}")
-    log(f"sampled near-ties: {ties}")
+    log(f"near-ties, all checked tokens: {ties}")
+    for m in MODES:
+        log(f"{m}, whole batches at every 25th step: {full[m]}")
 
     # Resume: restart SMEBU from the saved (b, m) and replay the second half; bit-exact.
     bd, md = to_dev(saved[0]), to_dev(saved[1])

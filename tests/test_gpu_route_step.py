@@ -193,3 +193,33 @@ def test_route_step_dispatch_at_tile_switch(T):
     check_counts(out.counts.cpu().numpy(), idx, wl.n_experts)
     check_dispatch(out.offsets.cpu().numpy(), out.perm.cpu().numpy(), out.inv_perm.cpu().numpy(), idx, wl.n_experts)
     log(f"T={T}: dispatch matches the oracle")
+
+
+@pytest.mark.parametrize("dispatch,update,zloss", [(True, True, False), (False, True, False), (False, False, True),
+                                                   (False, False, False), (True, False, True)])
+def test_step_end_event(dispatch, update, zloss):
+    """The third timing event takes the end of the step's last kernel (the scatter, the update,
+    the z-loss, or an empty kernel after a lone router kernel): it is never before the router
+    kernel's end, and timing changes no output."""
+    T, d, n_e, k = 3000, 512, 256, 4
+    _, x, w, b0 = make(T, d, n_e, k, seed=3)
+    xd = to_dev(x)
+    outs = []
+    for timed in (True, False):
+        step = elb.RouterStep(to_dev(w), to_dev(b0), torch.zeros(n_e, device="cuda"), k, T, update=update,
+                              dispatch=dispatch, want_zloss=zloss)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        if timed:
+            step.set_timing(*ev)
+        out = step(xd)
+        torch.cuda.synchronize()
+        if timed:
+            r, e = ev[0].elapsed_time(ev[1]), ev[0].elapsed_time(ev[2])
+            log(f"  dispatch={dispatch} update={update} zloss={zloss}: router {r * 1e3:.1f} us, step {e * 1e3:.1f} us")
+            assert 0.0 < r <= e < 100.0, (r, e)
+        got = [t.cpu().numpy() for t in (out.topk_idx, out.gates, step.bias)]
+        if dispatch:
+            got += [out.perm.cpu().numpy()]
+        outs.append(got)
+    for a, b in zip(*outs):
+        assert (a == b).all()

@@ -206,3 +206,23 @@ def test_determinism():
     c = run(x, w, b, 4)
     for u, v in zip(a, c):
         assert (u.view(np.uint32) == v.view(np.uint32)).all()
+
+
+@pytest.mark.parametrize("spread", [40.0, 1000.0])
+@pytest.mark.parametrize("kernel", ["mfma", "generic"])
+def test_wide_bias_spread(spread, kernel):
+    """A bias range far wider than SMEBU ever produces: the selection must still be exact to
+    the tie band.  48 experts sit near +spread/2 (jittered by 0.05), 48 near 0 and the rest near
+    -spread/2, so every token picks among the top group and the scores decide; a second bias
+    draws every b_i uniformly over the whole range."""
+    wl, x, w, _ = make(3000, 512, 256, 4, kind="clusters")
+    rng = np.random.default_rng(int(spread))
+    groups = np.repeat([0.5, 0.0, -0.5], [48, 48, 160])[rng.permutation(256)]
+    b1 = (groups * spread + rng.normal(0.0, 0.05, 256)).astype(np.float32)
+    b2 = rng.uniform(-spread / 2, spread / 2, 256).astype(np.float32)
+    for b in (b1, b2):
+        log(f"bias spread {float(b.max() - b.min()):.1f} kernel={kernel}")
+        idx, gates, counts, _ = run(x, w, b, 4, force_generic=(kernel == "generic"))
+        rep = compare_route(idx, gates, x, w, b, 4)
+        check_counts(counts, idx, 256)
+        log(f"  {rep}")

@@ -41,7 +41,7 @@ from ._lib import (  # noqa: F401
     lib,
 )
 
-__all__ = ["router_forward", "router_dispatch", "dispatch_workspace_bytes", "smebu_update", "smebu_update_layers",
+__all__ = ["router_forward", "router_dispatch", "router_dispatch_noalloc", "dispatch_workspace_bytes", "smebu_update", "smebu_update_layers",
            "maxvio", "zloss", "permute_rows", "unpermute_combine", "router_backward", "backward_workspace_bytes", "RouterStep", "StepOutputs", "version", "ElbError",
            "MODES"]
 
@@ -171,6 +171,28 @@ def router_dispatch(topk_idx: torch.Tensor, n_experts: int, *, workspace: torch.
     st = lib().elb_router_dispatch(_ptr(topk_idx), T, k, n_experts, _ptr(workspace), nbytes, _ptr(offsets),
                                    _ptr(perm), _ptr(inv), _stream(dev))
     check("elb_router_dispatch", st)
+    return offsets, perm, inv
+
+
+def router_dispatch_noalloc(topk_idx: torch.Tensor, n_experts: int, out: tuple):
+    """router_dispatch through the library's allocation-free entry point, into caller buffers
+    ``out`` = (offsets [N_r+1], perm [T*k], inv [T*k] or None), int32 on topk_idx's device.  The
+    library uses a static per-GPU workspace (8 MiB); calls overlapping on one GPU race."""
+    if not isinstance(topk_idx, torch.Tensor) or topk_idx.dim() != 2:
+        raise ValueError("topk_idx must be a [T, k] tensor")
+    T, k = topk_idx.shape
+    offsets, perm, inv = out
+    if offsets.numel() != n_experts + 1 or perm.numel() != T * k or (inv is not None and inv.numel() != T * k):
+        raise ValueError("router_dispatch_noalloc: out tensors have the wrong sizes")
+    _need(topk_idx, "topk_idx", torch.int32)
+    dev = topk_idx.device
+    _need(offsets, "offsets", torch.int32, dev)
+    _need(perm, "perm", torch.int32, dev)
+    if inv is not None:
+        _need(inv, "inv", torch.int32, dev)
+    st = lib().elb_router_dispatch_noalloc(_ptr(topk_idx), T, k, n_experts, _ptr(offsets), _ptr(perm), _ptr(inv),
+                                           _stream(dev))
+    check("elb_router_dispatch_noalloc", st)
     return offsets, perm, inv
 
 

@@ -45,6 +45,7 @@ SIGNATURES = {
     "elb_router_forward": (_I32, [_P, _I32, _I64, _I32, _P, _P, _I32, _I32, _U32, _P, _P, _P, _P, _P, _P]),
     "elb_dispatch_workspace_bytes": (_SZ, [_I64, _I32, _I32]),
     "elb_router_dispatch": (_I32, [_P, _I64, _I32, _I32, _P, _SZ, _P, _P, _P, _P]),
+    "elb_router_dispatch_noalloc": (_I32, [_P, _I64, _I32, _I32, _P, _P, _P, _P]),
     "elb_smebu_update": (_I32, [_P, _I32, BalanceParams, _P, _P, _P, _P, _P]),
     "elb_route_step": (_I32, [ctypes.POINTER(StepArgs), _P]),
     "elb_smebu_update_layers": (_I32, [_P, _I32, _I32, BalanceParams, _P, _P, _P, _P, _P]),

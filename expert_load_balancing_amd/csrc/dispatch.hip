@@ -27,8 +27,20 @@
 #include "device_common.hpp"
 #include "elb_kernels.h"
 
+#include <mutex>
+
+// The dispatch workspace of elb_router_dispatch_noalloc, for callers that cannot allocate: one
+// copy per GPU, held until the process ends.  Host code never passes this name to a kernel (in
+// host code it is a host-side stand-in, not the device address): dispatch_scratch() looks up
+// each device's own address once, with that device current, and the launches use that.
+static __device__ __align__(256) unsigned char scratch[elb::kDispatchScratchBytes];
+
 namespace elb {
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_addr[kMaxDevices];  // device address of `scratch` per device ordinal, set on first use
 
 constexpr int kThreads = kDispatchTile;  // one thread per token (per entry of a chunk)
 constexpr int kWaves = kThreads / 64;
@@ -180,6 +192,30 @@ hipError_t launch_scatter(const int32_t* idx, int64_t total, int n_experts, cons
 }
 
 }  // namespace
+
+hipError_t dispatch_scratch(hipStream_t stream, void** ptr) {
+  hipDevice_t dev = 0;
+  hipError_t err = hipStreamGetDevice(stream, &dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_addr[dev] == nullptr) {
+    int cur = 0;
+    if ((err = hipGetDevice(&cur)) != hipSuccess) return err;
+    if (cur != dev && (err = hipSetDevice(dev)) != hipSuccess) return err;
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t back = hipSetDevice(cur);
+      if (err == hipSuccess) err = back;
+    }
+    if (err != hipSuccess) return err;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    scratch_addr[dev] = p;
+  }
+  *ptr = scratch_addr[dev];
+  return hipSuccess;
+}
 
 DispatchGeom dispatch_geometry(int64_t T) {
   DispatchGeom g;

@@ -100,6 +100,22 @@ elb_status elb_router_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, in
   return from_hip(elb::launch_dispatch(topk_idx, T, k, n_experts, workspace, false, nullptr, offsets, perm, inv_perm, s));
 }
 
+elb_status elb_router_dispatch_noalloc(const int32_t* topk_idx, int64_t T, int32_t k, int32_t n_experts,
+                                       int32_t* offsets, int32_t* perm, int32_t* inv_perm, elb_stream_t stream) {
+  // The checks of elb_router_dispatch, with the static scratch standing in for the workspace.
+  if (offsets == nullptr) return ELB_ERR_NULL;
+  if (T > 0 && (topk_idx == nullptr || perm == nullptr)) return ELB_ERR_NULL;
+  if (T < 0 || k < 1 || k > 8 || n_experts < 1 || n_experts > 256) return ELB_ERR_SHAPE;
+  if (T * (int64_t)k >= (int64_t(1) << 31)) return ELB_ERR_SHAPE;
+  if (elb::dispatch_workspace_bytes(T, n_experts) > elb::kDispatchScratchBytes) return ELB_ERR_WORKSPACE;
+  if (!aligned(topk_idx, 4) || !aligned(offsets, 4) || !aligned(perm, 4) || !aligned(inv_perm, 4))
+    return ELB_ERR_ALIGN;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if (elb::dispatch_scratch(s, &ws) != hipSuccess) return ELB_ERR_LAUNCH;
+  return from_hip(elb::launch_dispatch(topk_idx, T, k, n_experts, ws, false, nullptr, offsets, perm, inv_perm, s));
+}
+
 elb_status elb_smebu_update(int32_t* counts, int32_t n_experts, elb_balance_params params, float* bias,
                             float* momentum, float* delta_b, float* maxvio, elb_stream_t stream) {
   const elb_status st = check_update(counts, n_experts, params, bias, momentum, delta_b, maxvio);

@@ -89,6 +89,10 @@ struct DispatchGeom {
 };
 DispatchGeom dispatch_geometry(int64_t T);
 size_t dispatch_workspace_bytes(int64_t T, int n_experts);
+// The static dispatch workspace of elb_router_dispatch_noalloc (dispatch.hip): its size, and its
+// device address on the device of `stream` (looked up once per device).
+constexpr size_t kDispatchScratchBytes = size_t(8) << 20;
+hipError_t dispatch_scratch(hipStream_t stream, void** ptr);
 // loads_ready: the router kernel already filled the loads table for this batch.
 // update: NULL, or a bias update to run beside the scatter (one extra workgroup).
 // ev_stop: NULL, or an event that takes the end time stamp of the dispatch's last kernel.

@@ -139,6 +139,23 @@ elb_status elb_router_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, in
                                int32_t* perm, int32_t* inv_perm, elb_stream_t stream);
 
 /*
+ * elb_router_dispatch for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same sort, the same
+ * outputs bit for bit, with no workspace argument.  Its workspace is a static device array of
+ * 8 MiB inside the library, one copy per GPU, held until the process ends; the call allocates
+ * nothing and frees nothing.  Sizes whose elb_dispatch_workspace_bytes exceeds 8 MiB (at
+ * n_experts = 256: more than 2,096,128 tokens) are refused with ELB_ERR_WORKSPACE.  The first
+ * call on a GPU looks up that GPU's copy (hipGetSymbolAddress, with the device of `stream`
+ * made current for the lookup).  Every call on one GPU shares its copy: calls that overlap on
+ * one GPU (on different streams, or from several threads without ordering) race and give
+ * wrong results.  Errors: ELB_ERR_NULL, ELB_ERR_SHAPE, ELB_ERR_WORKSPACE, ELB_ERR_ALIGN,
+ * ELB_ERR_LAUNCH (also when the lookup fails).
+ */
+elb_status elb_router_dispatch_noalloc(const int32_t* topk_idx, int64_t T, int32_t k,
+                                       int32_t n_experts, int32_t* offsets, int32_t* perm,
+                                       int32_t* inv_perm, elb_stream_t stream);
+
+/*
  * One expert-bias update from one optimizer step's loads (study note eq. (20)-(28)).
  *   counts   [n_experts] int32: n_i for the step.
  *   bias     [n_experts] fp32 in/out: b.

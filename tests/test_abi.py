@@ -296,3 +296,26 @@ def test_binding_checks_buffer_sizes_before_the_device():
     with pytest.raises(ValueError, match="GPU"):
         elb.router_forward(x, w, b, 4, out=(torch.zeros(10, 4, dtype=i32), torch.zeros(10, 4)),
                            counts=torch.zeros(256, dtype=i32))
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(offsets=None), NULL), (dict(idx=None), NULL), (dict(perm=None), NULL),
+    (dict(n=0), SHAPE), (dict(n=257), SHAPE), (dict(k=0), SHAPE), (dict(k=9), SHAPE), (dict(T=-5), SHAPE),
+    (dict(T=(1 << 31) // 8, k=8), SHAPE),  # T * k = 2^31: past the int32 positions
+    (dict(T=2_096_129), WORKSPACE),  # one token past what the 8 MiB static workspace holds at 256 experts
+    (dict(T=8_388_608, n=64, k=1), WORKSPACE),
+    (dict(offsets=FAKE + 2), ALIGN), (dict(inv=FAKE + 1), ALIGN),
+])
+def test_router_dispatch_noalloc_rejects(lib, kw, want):
+    """The allocation-free dispatch refuses what elb_router_dispatch refuses, and sizes past its
+    static workspace, before touching any device."""
+    a = dict(idx=FAKE, T=4096, k=4, n=256, offsets=FAKE, perm=FAKE, inv=None)
+    a.update(kw)
+    st = lib.elb_router_dispatch_noalloc(a["idx"], a["T"], a["k"], a["n"], a["offsets"], a["perm"], a["inv"], None)
+    assert st == want
+
+
+def test_noalloc_limit_matches_the_workspace_size(lib):
+    """The largest batch the static workspace holds at 256 experts: 2,096,128 tokens (8188 tiles)."""
+    assert lib.elb_dispatch_workspace_bytes(2_096_128, 4, 256) <= 8 << 20
+    assert lib.elb_dispatch_workspace_bytes(2_096_129, 4, 256) > 8 << 20

@@ -238,6 +238,10 @@ struct Stream {
   uint32_t voa[kDmaA], vob[kDmaB];
   uint32_t wave_off_a, wave_off_b, a_stage, b_stage;
   int nkb;
+  // Rotation of the k loop: stage j reads the operands' stage (j + rot) mod nkb (0 <= rot < nkb).
+  // Both operands rotate together, so the product is the same sum taken from another starting
+  // stage.  Workgroups with different rotations read different columns at the same moment.
+  int rot = 0;
   bool issues;  // this wave issues DMAs
   Slots sl;
 
@@ -262,6 +266,13 @@ struct Stream {
     b_stage = LB::stage_bytes(b_row_bytes);
   }
 
+  // Byte offset of logical stage v (< nkb) in the operand's k direction, after the rotation.
+  // Stages v >= nkb are the trailing dummies: their offset is never read.
+  __device__ __forceinline__ uint32_t phys(int v) const {
+    const int p = v + rot;
+    return (uint32_t)(p >= nkb ? p - nkb : p);
+  }
+
   // Stages 0..kPX-1 of B and 0..kPW-1 of A, issued in the same order the steady state uses
   // (A first, then B, per virtual iteration).
   __device__ __forceinline__ void prologue() {
@@ -269,9 +280,9 @@ struct Stream {
 #pragma unroll
     for (int vi = -kPX; vi < 0; ++vi) {
       if (vi + kPW >= 0)
-        dma_rows<AUX_A, kDmaA>(ar, none, sl.w((vi + kPW) % kNW) + wave_off_a, voa, (uint32_t)(vi + kPW) * a_stage,
+        dma_rows<AUX_A, kDmaA>(ar, none, sl.w((vi + kPW) % kNW) + wave_off_a, voa, phys(vi + kPW) * a_stage,
                         vi + kPW < nkb);
-      dma_rows<AUX_B, kDmaB>(br, none, sl.x((vi + kPX) % kNX) + wave_off_b, vob, (uint32_t)(vi + kPX) * b_stage,
+      dma_rows<AUX_B, kDmaB>(br, none, sl.x((vi + kPX) % kNX) + wave_off_b, vob, phys(vi + kPX) * b_stage,
                       vi + kPX < nkb);
     }
   }
@@ -321,10 +332,10 @@ struct Stream {
         // budget); the B DMAs are spread over the MFMA stream below, so that a DMA waiting for
         // room in the vector memory pipeline only delays MFMAs already queued.
         if constexpr (DMA) {
-          dma_rows<AUX_A, kDmaA>(ar, none, sl.w((u + kPW) % kNW) + wave_off_a, voa, (uint32_t)(j + kPW) * a_stage,
+          dma_rows<AUX_A, kDmaA>(ar, none, sl.w((u + kPW) % kNW) + wave_off_a, voa, phys(j + kPW) * a_stage,
                                  j + kPW < nkb);
           __builtin_amdgcn_sched_barrier(0);
-          dma_rows<AUX_B, kDmaB>(br, none, sl.x((u + kPX) % kNX) + wave_off_b, vob, (uint32_t)(j + kPX) * b_stage,
+          dma_rows<AUX_B, kDmaB>(br, none, sl.x((u + kPX) % kNX) + wave_off_b, vob, phys(j + kPX) * b_stage,
                                  j + kPX < nkb);
         }
         const unsigned char* ws = sl.w(u % kNW);

@@ -226,3 +226,28 @@ def test_wide_bias_spread(spread, kernel):
         rep = compare_route(idx, gates, x, w, b, 4)
         check_counts(counts, idx, 256)
         log(f"  {rep}")
+
+
+@pytest.mark.parametrize("T,d", [(3000, 2048), (20000, 4096), (40000, 4096), (40000, 2048)])
+def test_rotated_k_loop(T, d):
+    """Rows a multiple of 4 KiB apart: every workgroup starts its k loop at another stage (all
+    three tile sizes); routing and logits still match the oracle, and duplicated rows placed in
+    tiles with different starting stages still choose the same experts wherever the choice is
+    separated by more than the comparison's resolution."""
+    log(f"rotated k loop T={T} d={d}")
+    wl, x, w, b = make(T, d, 256, 4, kind="clusters")
+    x = x.copy()
+    src = np.array([0, 1, 2, 3, 5, 7])
+    dst = np.array([300, 700, 1201, 2500, T - 1, T // 2])  # other tiles: other starting stages
+    assert len(set(dst.tolist()) | set(src.tolist())) == 12
+    x[dst] = x[src]
+    idx, gates, counts, logits = run(x, w, b, 4)
+    rep = compare_route(idx, gates, x, w, b, 4)
+    check_counts(counts, idx, 256)
+    compare_logits(logits, x, w)
+    r = oracle.route(x[src], w, b, 4, keep=True)
+    q = np.sort(r.scores + b.astype(np.float64)[None, :], axis=1)[:, ::-1][:, :5]
+    sep = (np.diff(-q, axis=1) >= 1e-5).all(axis=1)
+    assert (idx[dst][sep] == idx[src][sep]).all()
+    assert np.allclose(logits[dst], logits[src], rtol=1e-5, atol=1e-5)
+    log(f"  {rep}")

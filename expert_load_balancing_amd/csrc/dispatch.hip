@@ -13,7 +13,9 @@
 //   totals [n_experts] int32.
 //  1. loads:   one workgroup per tile, LDS histogram.  Skipped when the MFMA router kernel
 //              already stored its own tile histogram in the table.
-//  2. scan:    one wave per expert scans its row in place and writes the expert's total.
+//  2. scan:    one wave per expert scans its row in place and writes the expert's total (and,
+//              in a routed step, adds it into the step's expert loads: the router kernel then
+//              leaves `counts` alone, which spares 256 contended global atomics per tile).
 //  3. scatter: one workgroup per tile, one pass.  With a bias update requested, one more
 //              workgroup runs it (balance_wave.hpp): the update reads only `counts`, which are
 //              final once the router kernel is done, and its few microseconds of dependent
@@ -77,7 +79,8 @@ __global__ __launch_bounds__(kThreads) void dispatch_loads_kernel(const int32_t*
 // Block e < n_experts scans row e.
 __global__ __launch_bounds__(64) void dispatch_scan_kernel(int32_t* __restrict__ loads, int64_t n_tiles,
                                                            int64_t stride, int n_experts,
-                                                           int32_t* __restrict__ totals) {
+                                                           int32_t* __restrict__ totals,
+                                                           int32_t* __restrict__ counts, int accumulate) {
   const int lane = threadIdx.x;
   int32_t* const row = loads + (int64_t)blockIdx.x * stride;
   int carry = 0;
@@ -95,7 +98,10 @@ __global__ __launch_bounds__(64) void dispatch_scan_kernel(int32_t* __restrict__
       *reinterpret_cast<i32x4*>(row + t0) = i32x4{excl, excl + v[0], excl + v[0] + v[1], excl + v[0] + v[1] + v[2]};
     carry += __shfl(incl, 63);
   }
-  if (lane == 0) totals[blockIdx.x] = carry;
+  if (lane == 0) {
+    totals[blockIdx.x] = carry;
+    if (counts != nullptr) counts[blockIdx.x] = (accumulate ? counts[blockIdx.x] : 0) + carry;
+  }
 }
 
 template <int K>
@@ -231,10 +237,11 @@ size_t dispatch_workspace_bytes(int64_t T, int n_experts) {
 }
 
 hipError_t launch_dispatch(const int32_t* idx, int64_t T, int k, int n_experts, void* workspace, bool loads_ready,
-                           const BalanceArgs* update, int32_t* offsets, int32_t* perm, int32_t* inv,
-                           hipStream_t stream, hipEvent_t ev_stop) {
+                           int32_t* counts, bool accumulate, const BalanceArgs* update, int32_t* offsets,
+                           int32_t* perm, int32_t* inv, hipStream_t stream, hipEvent_t ev_stop) {
   if (T == 0) {
-    const hipError_t err = launch_fill_i32(offsets, n_experts + 1, 0, stream);
+    hipError_t err = launch_fill_i32(offsets, n_experts + 1, 0, stream);
+    if (err == hipSuccess && counts != nullptr && !accumulate) err = launch_fill_i32(counts, n_experts, 0, stream);
     if (err != hipSuccess) return err;
     if (update != nullptr) return launch_balance(*update, stream, ev_stop);
     return ev_stop != nullptr ? launch_mark(ev_stop, stream) : hipSuccess;
@@ -250,7 +257,7 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t T, int k, int n_experts, 
     if (err != hipSuccess) return err;
   }
   err = launch(dispatch_scan_kernel, dim3((unsigned)n_experts), dim3(64), 0, stream, loads, g.n_tiles, g.stride,
-               n_experts, totals);
+               n_experts, totals, counts, accumulate ? 1 : 0);
   if (err != hipSuccess) return err;
   const int32_t* cl = loads;
   const int32_t* ct = totals;

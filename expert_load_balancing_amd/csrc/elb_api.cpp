@@ -97,7 +97,8 @@ elb_status elb_router_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, in
       check_dispatch(topk_idx, T, k, n_experts, workspace, workspace_bytes, offsets, perm, inv_perm);
   if (st != ELB_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  return from_hip(elb::launch_dispatch(topk_idx, T, k, n_experts, workspace, false, nullptr, offsets, perm, inv_perm, s));
+  return from_hip(elb::launch_dispatch(topk_idx, T, k, n_experts, workspace, false, nullptr, false, nullptr, offsets, perm,
+                                       inv_perm, s));
 }
 
 elb_status elb_router_dispatch_noalloc(const int32_t* topk_idx, int64_t T, int32_t k, int32_t n_experts,
@@ -113,7 +114,7 @@ elb_status elb_router_dispatch_noalloc(const int32_t* topk_idx, int64_t T, int32
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   void* ws = nullptr;
   if (elb::dispatch_scratch(s, &ws) != hipSuccess) return ELB_ERR_LAUNCH;
-  return from_hip(elb::launch_dispatch(topk_idx, T, k, n_experts, ws, false, nullptr, offsets, perm, inv_perm, s));
+  return from_hip(elb::launch_dispatch(topk_idx, T, k, n_experts, ws, false, nullptr, false, nullptr, offsets, perm, inv_perm, s));
 }
 
 elb_status elb_smebu_update(int32_t* counts, int32_t n_experts, elb_balance_params params, float* bias,
@@ -145,12 +146,15 @@ elb_status elb_route_step(const elb_step_args* args, elb_stream_t stream) {
   if (!aligned(a.zloss, 4)) return ELB_ERR_ALIGN;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (!(a.flags & ELB_ACCUMULATE_COUNTS)) {
+  const bool accumulate = (a.flags & ELB_ACCUMULATE_COUNTS) != 0;
+  // With a dispatch, the expert loads come from its scan over the per-tile loads (which it needs
+  // anyway), not from the router's global atomics; it also clears them for an empty batch.
+  if (!accumulate && !dispatch) {
     if (elb::launch_fill_i32(a.counts, a.n_experts, 0, s) != hipSuccess) return ELB_ERR_LAUNCH;
   }
   const elb::DispatchGeom g = elb::dispatch_geometry(a.T);
   elb::RouterArgs ra{a.x,     a.dtype,    a.T,      a.d,      a.w,     a.bias, a.n_experts,
-                     a.k,     a.flags,    a.topk_idx, a.gates, a.counts, a.logits, a.lse,
+                     a.k,     a.flags,    a.topk_idx, a.gates, dispatch ? nullptr : a.counts, a.logits, a.lse,
                      static_cast<int32_t*>(a.workspace), g.stride};
   const bool mfma = !(a.flags & ELB_FORCE_GENERIC) && elb::router_mfma_applies(ra);
   const bool loads_ready = dispatch && mfma && elb::router_mfma_full_tile(a.T);  // the router fills the table
@@ -178,7 +182,7 @@ elb_status elb_route_step(const elb_step_args* args, elb_stream_t stream) {
   const elb::BalanceArgs upd =
       balance_args(a.counts, a.n_experts, a.params, a.bias, a.momentum, a.delta_b, a.maxvio);
   if (!dispatch) return a.update != 0 ? from_hip(elb::launch_balance(upd, s, ev_end)) : ELB_OK;
-  return from_hip(elb::launch_dispatch(a.topk_idx, a.T, a.k, a.n_experts, a.workspace, loads_ready,
+  return from_hip(elb::launch_dispatch(a.topk_idx, a.T, a.k, a.n_experts, a.workspace, loads_ready, a.counts, accumulate,
                                        a.update != 0 ? &upd : nullptr, a.offsets, a.perm, a.inv_perm, s, ev_end));
 }
 

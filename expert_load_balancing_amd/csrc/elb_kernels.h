@@ -94,10 +94,12 @@ size_t dispatch_workspace_bytes(int64_t T, int n_experts);
 constexpr size_t kDispatchScratchBytes = size_t(8) << 20;
 hipError_t dispatch_scratch(hipStream_t stream, void** ptr);
 // loads_ready: the router kernel already filled the loads table for this batch.
+// counts: NULL, or the expert loads that the scan sets to (accumulate: adds) this batch's totals.
 // update: NULL, or a bias update to run beside the scatter (one extra workgroup).
 // ev_stop: NULL, or an event that takes the end time stamp of the dispatch's last kernel.
 hipError_t launch_dispatch(const int32_t* idx, int64_t T, int k, int n_experts, void* workspace, bool loads_ready,
-                           const BalanceArgs* update, int32_t* offsets, int32_t* perm, int32_t* inv,
+                           int32_t* counts, bool accumulate, const BalanceArgs* update, int32_t* offsets,
+                           int32_t* perm, int32_t* inv,
                            hipStream_t stream, hipEvent_t ev_stop = nullptr);
 
 // ev_stop (optional): an event that takes the kernel's end time stamp.

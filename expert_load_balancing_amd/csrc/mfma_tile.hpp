@@ -18,9 +18,11 @@
 //
 // Memory pipeline: k is consumed in stages of 64 elements (128 bytes of every row: a full HBM
 //   line per row per visit; 64-byte visits stream markedly slower because all workgroups touch
-//   their rows 2*K bytes apart at once).  The B stream runs 2 stages ahead in a ring of 3 LDS
-//   slots, the A stream 1 stage ahead in a ring of 2 (A is meant to be the operand that stays in
-//   L2, well within one stage).  The five 32 KiB slots fill the 160 KiB LDS.  Rows past the end
+//   their rows 2*K bytes apart at once).  By default the B stream runs 2 stages ahead in a ring
+//   of 3 LDS slots, the A stream 1 stage ahead in a ring of 2 (A is meant to be the operand that
+//   stays in L2, well within one stage): the five 32 KiB slots fill the 160 KiB LDS.  Tiles with
+//   fewer B rows have shorter stages and smaller B slots, and take deeper rings (NXR, NWR), so
+//   that the prefetch still spans the memory latency.  Rows past the end
 //   of an operand fall outside its buffer range and arrive as zeros.  Every wave waits for its
 //   own DMAs with an explicit vmcnt budget, then one barrier per stage publishes the slot to all
 //   waves and frees the slot the next DMA overwrites.  Barriers carry no memory fence: a fence
@@ -108,12 +110,19 @@ __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, __amdgpu_buff
 // whole 256-byte bank window (rows r and r + 1 already sit in different 128-byte halves).
 __device__ __forceinline__ constexpr int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-// The five LDS slots (declared __shared__ by the kernel, each kSlot bytes, 1 KiB aligned).
+// The LDS ring slots (declared __shared__ by the kernel, 1 KiB aligned): up to four for the B
+// stream (x) and four for the A stream (w); x3, w2, w3 only with deeper rings.
 struct Slots {
-  unsigned char *x0, *x1, *x2, *w0, *w1;
-  __device__ __forceinline__ unsigned char* x(int i) const { return i == 0 ? x0 : i == 1 ? x1 : x2; }
-  __device__ __forceinline__ unsigned char* w(int i) const { return i == 0 ? w0 : w1; }
+  unsigned char *x0, *x1, *x2, *w0, *w1, *x3 = nullptr, *w2 = nullptr, *w3 = nullptr;
+  __device__ __forceinline__ unsigned char* x(int i) const { return i == 0 ? x0 : i == 1 ? x1 : i == 2 ? x2 : x3; }
+  __device__ __forceinline__ unsigned char* w(int i) const { return i == 0 ? w0 : i == 1 ? w1 : i == 2 ? w2 : w3; }
 };
+
+constexpr int ring_lcm(int a, int b) {
+  int l = a;
+  while (l % b != 0) l += a;
+  return l;
+}
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
@@ -214,9 +223,17 @@ struct KRows {
 // and issues MFMAs, so no DMA that waits for room in the vector memory pipeline ever holds up
 // its MFMAs (a wave issues in order).  TG: token groups (waves / ES); TG = 2 (with ES = 2, NB = 1)
 // makes a 4-wave tile of 64 B rows, for batches too small to give every CU even 128 B rows.
+// NXR / NWR: slots of the B and A rings (each stream runs one stage fewer ahead); a B slot holds
+// the tile's 32 TG NB rows (rows-contiguous layout), an A slot 256 rows.
 template <int AUX_A, int AUX_B, class LA = RowsK, class LB = RowsK, int NB = kNB, int ES = 1, bool PR = false,
-          int TG = kWaves>
+          int TG = kWaves, int NXR = kNX, int NWR = kNW>
 struct Stream {
+  static constexpr int kNXr = NXR, kPXr = NXR - 1, kNWr = NWR, kPWr = NWR - 1;
+  static constexpr int kUnr = ring_lcm(NXR, NWR);  // slots are compile-time constants in the loop
+  static constexpr int kSlotB = LB::kReads == 1 ? 32 * TG * NB * kRowB : kSlot;  // bytes of a B slot
+  static_assert(NXR + NWR <= 8 && NXR <= 4 && NWR <= 4 && NXR >= 2 && NWR >= 2, "ring shape");
+  static_assert(NXR * kSlotB + NWR * kSlot <= 160 * 1024, "LDS");
+  static_assert(kPXr >= kPWr, "the vmcnt budget assumes the B stream runs at least as far ahead");
   static_assert(NB == kNB || (NB == 1 && LB::kReads == 1), "a 128-row B tile is laid out rows-contiguous-in-k");
   // Eight waves sharing the DMAs split a slot over 8: only rows-contiguous layouts lay out that way
   // (with PR four waves issue them, as in the 4-wave tile).
@@ -232,8 +249,8 @@ struct Stream {
   static constexpr int kDmaA = kDma * kWaves / kSharers;
   static constexpr int kDmaB = TG * NB * 4 / kSharers;
   // VMEM instructions a wave issues after the DMAs of stage j's A rows, when it must have stage
-  // j: the B DMAs of the same iteration, then (kPW - 1) full iterations.
-  static constexpr int kBudget = kDmaB + (kDmaA + kDmaB) * (kPW - 1);
+  // j: the B DMAs of the same iteration, then (kPWr - 1) full iterations.
+  static constexpr int kBudget = kDmaB + (kDmaA + kDmaB) * (kPWr - 1);
   __amdgpu_buffer_rsrc_t ar, br, none;
   uint32_t voa[kDmaA], vob[kDmaB];
   uint32_t wave_off_a, wave_off_b, a_stage, b_stage;
@@ -273,17 +290,17 @@ struct Stream {
     return (uint32_t)(p >= nkb ? p - nkb : p);
   }
 
-  // Stages 0..kPX-1 of B and 0..kPW-1 of A, issued in the same order the steady state uses
+  // Stages 0..kPXr-1 of B and 0..kPWr-1 of A, issued in the same order the steady state uses
   // (A first, then B, per virtual iteration).
   __device__ __forceinline__ void prologue() {
     if (!issues) return;
 #pragma unroll
-    for (int vi = -kPX; vi < 0; ++vi) {
-      if (vi + kPW >= 0)
-        dma_rows<AUX_A, kDmaA>(ar, none, sl.w((vi + kPW) % kNW) + wave_off_a, voa, phys(vi + kPW) * a_stage,
-                        vi + kPW < nkb);
-      dma_rows<AUX_B, kDmaB>(br, none, sl.x((vi + kPX) % kNX) + wave_off_b, vob, phys(vi + kPX) * b_stage,
-                      vi + kPX < nkb);
+    for (int vi = -kPXr; vi < 0; ++vi) {
+      if (vi + kPWr >= 0)
+        dma_rows<AUX_A, kDmaA>(ar, none, sl.w((vi + kPWr) % kNWr) + wave_off_a, voa, phys(vi + kPWr) * a_stage,
+                               vi + kPWr < nkb);
+      dma_rows<AUX_B, kDmaB>(br, none, sl.x((vi + kPXr) % kNXr) + wave_off_b, vob, phys(vi + kPXr) * b_stage,
+                             vi + kPXr < nkb);
     }
   }
 
@@ -321,7 +338,7 @@ struct Stream {
     int j0 = 0;
     do {
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+      for (int u = 0; u < kUnr; ++u) {
         const int j = j0 + u;
         if (j >= nkb) break;
         // Own DMAs of stage j are done; after the barrier everyone's are, and every wave has
@@ -332,14 +349,14 @@ struct Stream {
         // budget); the B DMAs are spread over the MFMA stream below, so that a DMA waiting for
         // room in the vector memory pipeline only delays MFMAs already queued.
         if constexpr (DMA) {
-          dma_rows<AUX_A, kDmaA>(ar, none, sl.w((u + kPW) % kNW) + wave_off_a, voa, phys(j + kPW) * a_stage,
-                                 j + kPW < nkb);
+          dma_rows<AUX_A, kDmaA>(ar, none, sl.w((u + kPWr) % kNWr) + wave_off_a, voa, phys(j + kPWr) * a_stage,
+                                 j + kPWr < nkb);
           __builtin_amdgcn_sched_barrier(0);
-          dma_rows<AUX_B, kDmaB>(br, none, sl.x((u + kPX) % kNX) + wave_off_b, vob, phys(j + kPX) * b_stage,
-                                 j + kPX < nkb);
+          dma_rows<AUX_B, kDmaB>(br, none, sl.x((u + kPXr) % kNXr) + wave_off_b, vob, phys(j + kPXr) * b_stage,
+                                 j + kPXr < nkb);
         }
-        const unsigned char* ws = sl.w(u % kNW);
-        const unsigned char* xs = sl.x(u % kNX);
+        const unsigned char* ws = sl.w(u % kNWr);
+        const unsigned char* xs = sl.x(u % kNXr);
         // Operand fragments are double-buffered: the LDS reads of k-step s + 1 go out before
         // the 16 MFMAs of k-step s, so their latency hides behind 512 MFMA cycles (one wave per
         // SIMD has no other wave to hide it).
@@ -387,7 +404,7 @@ struct Stream {
           if (s + 2 < kKSteps) __builtin_amdgcn_sched_group_barrier(0x100, kReadsStep, 0);  // DS reads, step s + 2
         }
       }
-      j0 += kUnroll;
+      j0 += kUnr;
     } while (j0 < nkb);
 
     // Drain the trailing dummy DMAs (they write slots the caller may reuse) and let every wave

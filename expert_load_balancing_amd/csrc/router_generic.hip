@@ -149,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void router_generic_kernel(const Tin* __r
     }
   }
   __syncthreads();
-  if (live && hist[tid] != 0) atomicAdd(&counts[tid], hist[tid]);
+  if (live && counts != nullptr && hist[tid] != 0) atomicAdd(&counts[tid], hist[tid]);
 }
 
 }  // namespace

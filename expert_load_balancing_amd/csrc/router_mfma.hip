@@ -98,33 +98,66 @@ __device__ __forceinline__ float sigmoid_fast(float z) {
 // lane-local slot in the low bits, re-keyed with 255 - expert before the merges), parks its
 // scores, and leaves its K keys (and, with EXTRA, its log-sum-exp partial) in LDS; after a
 // barrier one wave of each pair (eh = block parity) merges the partner's K keys and writes the
-// token's indices, gates and histogram counts.  The key addends (key_bias) are in ws1[0..1 KiB),
-// the histogram in ws1[1..2 KiB).
+// token's indices, gates and histogram counts.  The key addends (key_bias) are in scratch[0..1 KiB),
+// the histogram in scratch[1..2 KiB), the exchanged keys and log-sum-exp partials after them
+// (12 KiB in all); each wave parks its scores in its own 16 KiB region park[wave].
+// The pointers carry the LDS address space, so that every access through them stays an LDS
+// instruction (a generic pointer would make them flat accesses, which also count as vector
+// memory operations and wait behind the DMAs in flight).
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) float lds_f32;
+__device__ __forceinline__ lds_u8* to_lds(unsigned char* p) { return (lds_u8*)p; }
+
+// This wave's park, the two parks of its wave pair (waves 2 tq and 2 tq + 1: the gate lookup
+// reads one of them per expert half), and the scratch region.  All wave-uniform.
+struct Parks {
+  lds_u8* mine;
+  lds_u8* pair[2];
+  lds_u8* scratch;
+};
+
+// The per-wave park regions of a tile (8 of 16 KiB), chosen with wave-uniform selects.
+__device__ __forceinline__ unsigned char* park_region(int v, unsigned char* p0, unsigned char* p1,
+                                                      unsigned char* p2, unsigned char* p3, unsigned char* p4,
+                                                      unsigned char* p5, unsigned char* p6, unsigned char* p7) {
+  return v == 0 ? p0 : v == 1 ? p1 : v == 2 ? p2 : v == 3 ? p3 : v == 4 ? p4 : v == 5 ? p5 : v == 6 ? p6 : p7;
+}
+
+__device__ __forceinline__ Parks make_parks(int wave, unsigned char* scratch, unsigned char* p0, unsigned char* p1,
+                                            unsigned char* p2, unsigned char* p3, unsigned char* p4,
+                                            unsigned char* p5, unsigned char* p6, unsigned char* p7) {
+  Parks k;
+  k.mine = to_lds(park_region(wave, p0, p1, p2, p3, p4, p5, p6, p7));
+  k.pair[0] = to_lds(park_region(wave & ~1, p0, p1, p2, p3, p4, p5, p6, p7));
+  k.pair[1] = to_lds(park_region(wave | 1, p0, p1, p2, p3, p4, p5, p6, p7));
+  k.scratch = to_lds(scratch);
+  return k;
+}
+
 template <int K, bool FULL, bool EXTRA, int NB>
 __device__ __forceinline__ void epilogue_split(const f32x16 (&acc)[kMB / 2][NB], int tid, int wave, int lane,
                                                int64_t row0, int64_t T, int n_experts, int normalize, float kbias, float kscale,
-                                               unsigned char* xs0, unsigned char* xs1, unsigned char* xs2,
-                                               unsigned char* ws0, unsigned char* ws1, int32_t* __restrict__ idx_out,
+                                               const Parks& pk_lds, int32_t* __restrict__ idx_out,
                                                float* __restrict__ gates_out, float* __restrict__ logits,
                                                float* __restrict__ lse) {
   constexpr int kMBw = kMB / 2;
   const int h = lane >> 5;
   const int l32 = lane & 31;
   const int eh = wave & 1, tq = wave >> 1;
-  float* const kb_lds = reinterpret_cast<float*>(ws1);
-  int* const hist = reinterpret_cast<int*>(ws1 + 1024);
-  uint32_t* const xkey = reinterpret_cast<uint32_t*>(ws1 + 2048);             // [8 waves][32 tokens][8]
-  float2* const xlse = reinterpret_cast<float2*>(ws1 + 2048 + 8 * 32 * 8 * 4);  // [8 waves][32 tokens]
+  lds_u8* const scr = pk_lds.scratch;
+  typedef __attribute__((address_space(3))) int lds_i32;
+  typedef __attribute__((address_space(3))) uint32_t lds_u32;
+  typedef __attribute__((address_space(3))) f32x4 lds_f4;
+  lds_f32* const kb_lds = (lds_f32*)scr;
+  lds_i32* const hist = (lds_i32*)(scr + 1024);
+  lds_u32* const xkey = (lds_u32*)(scr + 2048);                   // [8 waves][32 tokens][8]
+  lds_f32* const xlse = (lds_f32*)(scr + 2048 + 8 * 32 * 8 * 4);  // [8 waves][32 tokens][2]
   if (tid < kExp) {
     kb_lds[tid] = tid < n_experts ? kbias : 0.0f;
     hist[tid] = 0;
   }
-  // Parks: wave v's scores in the 16 KiB half (v & 1) of slot v / 2, [16 groups][64 lanes][4].
-  auto park_of = [&](int v) {
-    unsigned char* const sl = (v >> 1) == 0 ? xs0 : (v >> 1) == 1 ? xs1 : (v >> 1) == 2 ? xs2 : ws0;
-    return reinterpret_cast<float*>(sl + (v & 1) * 16384);
-  };
-  float* const park = park_of(wave);
+  // Parks: wave v's scores in its region, [16 groups][64 lanes][4].
+  lds_f32* const park = (lds_f32*)pk_lds.mine;
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   bare_barrier();
 #pragma unroll
@@ -138,7 +171,7 @@ __device__ __forceinline__ void epilogue_split(const f32x16 (&acc)[kMB / 2][NB],
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int e0 = 128 * eh + mb * 32 + g * 8 + 4 * h;
-        const f32x4 kb = *reinterpret_cast<const f32x4*>(kb_lds + e0);
+        const f32x4 kb = *(const lds_f4*)(kb_lds + e0);
         f32x4 sv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -148,7 +181,7 @@ __device__ __forceinline__ void epilogue_split(const f32x16 (&acc)[kMB / 2][NB],
           const uint32_t key = sel_key(sc, kscale, kb[r], slot_id);
           topk_insert<K>(top, FULL || e0 + r < n_experts ? key : 0u);
         }
-        *reinterpret_cast<f32x4*>(park + ((mb * 4 + g) * 64 + lane) * 4) = sv;
+        *(lds_f4*)(park + ((mb * 4 + g) * 64 + lane) * 4) = sv;
       }
     }
     // Re-key with the global expert id, merge with lane ^ 32 (the wave's other 64 experts).
@@ -202,7 +235,10 @@ __device__ __forceinline__ void epilogue_split(const f32x16 (&acc)[kMB / 2][NB],
         sum = (m == mm ? sum : sum * __builtin_amdgcn_exp2f((m - mm) * kLog2e)) +
               (m2 == mm ? sum2 : sum2 * __builtin_amdgcn_exp2f((m2 - mm) * kLog2e));
         m = mm;
-        if (h == 0) xlse[wave * 32 + l32] = float2{m, sum};
+        if (h == 0) {
+          xlse[(wave * 32 + l32) * 2] = m;
+          xlse[(wave * 32 + l32) * 2 + 1] = sum;
+        }
       }
     }
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
@@ -219,7 +255,7 @@ __device__ __forceinline__ void epilogue_split(const f32x16 (&acc)[kMB / 2][NB],
         for (int j = 0; j < K; ++j) {
           e[j] = 255 - (int)(top[j] & 0xFFu);
           const int el = e[j] & 127;
-          const float* const pk = park_of(2 * tq + (e[j] >> 7));
+          const lds_f32* const pk = (const lds_f32*)((e[j] >> 7) ? pk_lds.pair[1] : pk_lds.pair[0]);
           sg[j] = pk[(((el >> 5) * 4 + ((el & 31) >> 3)) * 64 + l32 + 32 * ((el >> 2) & 1)) * 4 + (el & 3)];
           ssum += sg[j];
         }
@@ -231,7 +267,7 @@ __device__ __forceinline__ void epilogue_split(const f32x16 (&acc)[kMB / 2][NB],
             for (int j = 0; j < K; ++j) idx_out[t * K + j] = e[j];
           }
 #pragma unroll
-          for (int j = 0; j < K; ++j) atomicAdd(&hist[e[j]], 1);
+          for (int j = 0; j < K; ++j) __hip_atomic_fetch_add(&hist[e[j]], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         } else {
           const float inv = normalize ? 1.0f / ssum : 1.0f;
           if constexpr (K == 4) {
@@ -243,7 +279,7 @@ __device__ __forceinline__ void epilogue_split(const f32x16 (&acc)[kMB / 2][NB],
         }
         if constexpr (EXTRA) {
           if (lse != nullptr && h == 0) {
-            const float2 o = xlse[partner * 32 + l32];
+            const float2 o{xlse[(partner * 32 + l32) * 2], xlse[(partner * 32 + l32) * 2 + 1]};
             const float mm = fmaxf(m, o.x);
             const float tot = (m == mm ? sum : sum * __builtin_amdgcn_exp2f((m - mm) * kLog2e)) +
                               (o.x == mm ? o.y : o.y * __builtin_amdgcn_exp2f((o.x - mm) * kLog2e));
@@ -257,18 +293,23 @@ __device__ __forceinline__ void epilogue_split(const f32x16 (&acc)[kMB / 2][NB],
   }
 }
 
+// The ring slots fill the LDS; the epilogue reuses them once the ring drains.  The full tile
+// (NB = 2): tokens 3 x 32 KiB, weights 2 x 32 KiB.  The smaller tiles have shorter stages and
+// take deeper rings: 128 tokens 4 x 16 KiB + 3 x 32 KiB, 64 tokens 4 x 8 KiB + 4 x 32 KiB.
+template <int NB, int TG>
+struct Ring {
+  static constexpr int NXR = NB == kNB ? kNX : 4;
+  static constexpr int NWR = NB == kNB ? kNW : (TG == kWaves ? 3 : 4);
+};
+
 // NB: 32-token blocks per wave pair (tile of 128 NB tokens).  8 waves, two per SIMD: each pair
 // shares a token range, and each wave of it holds 128 of the 256 experts.
 template <int K, bool FULL, bool EXTRA, int NB, int TG>
-__global__ __launch_bounds__(TG * 128) __attribute__((amdgpu_waves_per_eu(2, 2))) void router_mfma_kernel(
+__device__ __forceinline__ void router_body(Slots slots, Parks pk,
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const float* __restrict__ bias, int64_t T, int d,
     int n_experts, int normalize, int32_t* __restrict__ idx_out, float* __restrict__ gates_out,
     int32_t* __restrict__ counts, float* __restrict__ logits, float* __restrict__ lse,
     int32_t* __restrict__ tile_loads, int64_t loads_stride) {
-  // The five ring slots are the whole LDS; the epilogue reuses them once the ring drains.
-  __shared__ __attribute__((aligned(1024))) unsigned char xs0[kSlot], xs1[kSlot], xs2[kSlot];
-  __shared__ __attribute__((aligned(1024))) unsigned char ws0[kSlot], ws1[kSlot];
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps LDS bases in SGPRs
@@ -281,12 +322,13 @@ __global__ __launch_bounds__(TG * 128) __attribute__((amdgpu_waves_per_eu(2, 2))
   float bq[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) bq[c] = lane + 64 * c < n_experts ? bias[lane + 64 * c] : __builtin_nanf("");
+  const float braw = tid < n_experts ? bias[tid] : 0.0f;
 
   // ---- operand streams: start the DMA ring (A = weights, B = this tile's tokens) ----
   const uint32_t row_bytes = (uint32_t)d * 2u;
-  Stream<kAuxCached, kAuxStream, RowsK, RowsK, NB, 2, TG == kWaves, TG> st;
+  Stream<kAuxCached, kAuxStream, RowsK, RowsK, NB, 2, TG == kWaves, TG, Ring<NB, TG>::NXR, Ring<NB, TG>::NWR> st;
   st.init(w, (uint32_t)n_experts * row_bytes, row_bytes, x + row0 * d, (uint32_t)rows * row_bytes, row_bytes,
-          d / kBK, wave, lane, Slots{xs0, xs1, xs2, ws0, ws1});
+          d / kBK, wave, lane, slots);
   // Rows a multiple of 4 KiB apart: every workgroup's rows share their low 12 address bits, so
   // workgroups in step would all read the same columns at once, which concentrates the traffic on
   // a few memory channels (the token stream alone ran at 5.4 instead of 7 TB/s at d = 4096).
@@ -294,7 +336,12 @@ __global__ __launch_bounds__(TG * 128) __attribute__((amdgpu_waves_per_eu(2, 2))
   if (row_bytes % 4096u == 0) st.rot = (int)(blockIdx.x % (uint32_t)(d / kBK));
   st.prologue();
 
+  f32x16 acc[kMB / 2][NB];
+  st.run(acc, wave, lane);
+
   // ---- selection key scaling from min b and max b (fminf / fmaxf skip the NaN padding) ----
+  // Only the epilogue needs it: done after the main loop, so that no wait for the bias loads
+  // drains the DMA prologue (the loads were issued first and landed long ago).
   float mn = fminf(fminf(bq[0], bq[1]), fminf(bq[2], bq[3]));
   float mx = fmaxf(fmaxf(bq[0], bq[1]), fmaxf(bq[2], bq[3]));
 #pragma unroll
@@ -303,22 +350,54 @@ __global__ __launch_bounds__(TG * 128) __attribute__((amdgpu_waves_per_eu(2, 2))
     mx = fmaxf(mx, __shfl_xor(mx, off));
   }
   const float kscale = key_scale(mn, mx);  // identical in every wave: min and max are exact
-  const float kbias = tid < n_experts ? key_bias(bias[tid], mn, kscale) : 0.0f;
+  const float kbias = tid < n_experts ? key_bias(braw, mn, kscale) : 0.0f;
+  epilogue_split<K, FULL, EXTRA, NB>(acc, tid, wave, lane, row0, T, n_experts, normalize, kbias, kscale, pk, idx_out,
+                                     gates_out, logits, lse);
 
-  f32x16 acc[kMB / 2][NB];
-  st.run(acc, wave, lane);
-  epilogue_split<K, FULL, EXTRA, NB>(acc, tid, wave, lane, row0, T, n_experts, normalize, kbias, kscale, xs0, xs1,
-                                     xs2, ws0, ws1, idx_out, gates_out, logits, lse);
-
-  int* const hist = reinterpret_cast<int*>(ws1 + 1024);
+  __attribute__((address_space(3))) int* const hist = (__attribute__((address_space(3))) int*)(pk.scratch + 1024);
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   bare_barrier();
   if (tid < n_experts) {
     const int n = hist[tid];
-    if (n != 0) atomicAdd(&counts[tid], n);
+    // No counts in a routed step with dispatch: the dispatch scan sums the tile loads into them.
+    if (counts != nullptr && n != 0) atomicAdd(&counts[tid], n);
     // This tile's loads for the dispatch scan (the full tile is the dispatch tile; the launcher
     // passes no table with the half tile).
     if (NB == kNB && tile_loads != nullptr) tile_loads[(int64_t)tid * loads_stride + blockIdx.x] = n;
+  }
+}
+
+template <int K, bool FULL, bool EXTRA, int NB, int TG>
+__global__ __launch_bounds__(TG * 128) __attribute__((amdgpu_waves_per_eu(2, 2))) void router_mfma_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const float* __restrict__ bias, int64_t T, int d,
+    int n_experts, int normalize, int32_t* __restrict__ idx_out, float* __restrict__ gates_out,
+    int32_t* __restrict__ counts, float* __restrict__ logits, float* __restrict__ lse,
+    int32_t* __restrict__ tile_loads, int64_t loads_stride) {
+  // Each tile declares its own ring slots (distinct arrays: the compiler tracks which DMA fills
+  // which slot), then the score parks (16 KiB per wave) and the epilogue's scratch in slots the
+  // drained ring leaves.
+  constexpr int XS = 32 * TG * NB * kRowB;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if constexpr (NB == kNB) {
+    __shared__ __attribute__((aligned(1024))) unsigned char xs0[XS], xs1[XS], xs2[XS], ws0[kSlot], ws1[kSlot];
+    router_body<K, FULL, EXTRA, NB, TG>(
+        Slots{xs0, xs1, xs2, ws0, ws1},
+        make_parks(wave, ws1, xs0, xs0 + 16384, xs1, xs1 + 16384, xs2, xs2 + 16384, ws0, ws0 + 16384), x, w, bias, T, d,
+        n_experts, normalize, idx_out, gates_out, counts, logits, lse, tile_loads, loads_stride);
+  } else if constexpr (TG == kWaves) {
+    __shared__ __attribute__((aligned(1024))) unsigned char xs0[XS], xs1[XS], xs2[XS], xs3[XS];
+    __shared__ __attribute__((aligned(1024))) unsigned char ws0[kSlot], ws1[kSlot], ws2[kSlot];
+    router_body<K, FULL, EXTRA, NB, TG>(
+        Slots{xs0, xs1, xs2, ws0, ws1, xs3, ws2},
+        make_parks(wave, xs2, ws0, ws0 + 16384, ws1, ws1 + 16384, ws2, ws2 + 16384, xs0, xs1), x, w, bias, T, d,
+        n_experts, normalize, idx_out, gates_out, counts, logits, lse, tile_loads, loads_stride);
+  } else {
+    __shared__ __attribute__((aligned(1024))) unsigned char xs0[XS], xs1[XS], xs2[XS], xs3[XS];
+    __shared__ __attribute__((aligned(1024))) unsigned char ws0[kSlot], ws1[kSlot], ws2[kSlot], ws3[kSlot];
+    router_body<K, FULL, EXTRA, NB, TG>(
+        Slots{xs0, xs1, xs2, ws0, ws1, xs3, ws2, ws3},
+        make_parks(wave, ws2, ws0, ws0 + 16384, ws1, ws1 + 16384, ws0, ws0, ws0, ws0), x, w, bias, T, d,
+        n_experts, normalize, idx_out, gates_out, counts, logits, lse, tile_loads, loads_stride);
   }
 }
 

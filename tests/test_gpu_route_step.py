@@ -223,3 +223,28 @@ def test_step_end_event(dispatch, update, zloss):
         outs.append(got)
     for a, b in zip(*outs):
         assert (a == b).all()
+
+
+@pytest.mark.parametrize("T,dtype", [(3000, "bf16"), (20000, "bf16"), (40000, "bf16"), (1000, "f32"), (0, "bf16")])
+def test_step_counts_without_accumulate(T, dtype):
+    """Without ELB_ACCUMULATE_COUNTS a step with a dispatch sets the loads to this batch's (its
+    scan writes them over whatever `counts` held; an empty batch leaves zeros), on the 256-token
+    tile that fills the loads table, on the 64- and 128-token tiles and on the fp32 generic kernel."""
+    n_e, k = 256, 4
+    wl = datagen.WORKLOADS["large"].replace(T=max(T, 1), d=128, n_experts=n_e, k=k, dtype=dtype, seed=T + 11,
+                                            n_clusters=8)
+    x, w, b = datagen.tokens(wl)[:T], datagen.router_weight(wl), datagen.initial_bias(wl)
+    step = elb.RouterStep(to_dev(w), to_dev(b), None, k, max(T, 1), update=False)
+    step._args.flags &= ~elb.ELB_ACCUMULATE_COUNTS
+    for it in range(2):
+        step.counts.fill_(12345 + it)  # stale loads that the step must not add to
+        out = step(to_dev(x).contiguous())
+        torch.cuda.synchronize()
+        idx = out.topk_idx.cpu().numpy()
+        got = out.counts.cpu().numpy()
+        assert np.array_equal(got, np.bincount(idx.ravel(), minlength=n_e)), f"call {it}: loads differ"
+        if T > 0:
+            check_dispatch(out.offsets.cpu().numpy(), out.perm.cpu().numpy(), out.inv_perm.cpu().numpy(), idx, n_e)
+        else:
+            assert (got == 0).all() and (out.offsets.cpu().numpy() == 0).all()
+    log(f"T={T} {dtype}: loads set, not accumulated")

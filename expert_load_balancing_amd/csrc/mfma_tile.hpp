@@ -222,7 +222,9 @@ struct KRows {
 // per SIMD) issue the DMAs, twice their share each; the other wave of each SIMD only reads LDS
 // and issues MFMAs, so no DMA that waits for room in the vector memory pipeline ever holds up
 // its MFMAs (a wave issues in order).  TG: token groups (waves / ES); TG = 2 (with ES = 2, NB = 1)
-// makes a 4-wave tile of 64 B rows, for batches too small to give every CU even 128 B rows.
+// makes a 4-wave tile of 64 B rows, for batches too small to give every CU even 128 B rows; with
+// PR it has 4 more waves (kWaves .. 2 kWaves - 1) that only issue the DMAs and hold no product,
+// so that each SIMD again pairs a multiplying wave with a DMA-issuing one.
 // NXR / NWR: slots of the B and A rings (each stream runs one stage fewer ahead); a B slot holds
 // the tile's 32 TG NB rows (rows-contiguous layout), an A slot 256 rows.
 template <int AUX_A, int AUX_B, class LA = RowsK, class LB = RowsK, int NB = kNB, int ES = 1, bool PR = false,
@@ -238,7 +240,7 @@ struct Stream {
   // Eight waves sharing the DMAs split a slot over 8: only rows-contiguous layouts lay out that way
   // (with PR four waves issue them, as in the 4-wave tile).
   static_assert(ES == 1 || (ES == 2 && (PR || (LA::kReads == 1 && LB::kReads == 1))), "the 8-wave DMA split");
-  static_assert(!PR || (ES == 2 && TG == kWaves), "DMA-issuing waves need a second wave per SIMD");
+  static_assert(!PR || (ES == 2 && (TG == kWaves || TG == 2)), "DMA-issuing waves need a second wave per SIMD");
   static_assert(TG == kWaves || (TG == 2 && ES == 2 && NB == 1 && LA::kReads == 1 && LB::kReads == 1),
                 "the 64-row B tile: 4 waves, rows-contiguous-in-k");
   static constexpr int kWavesS = TG * ES;
@@ -248,9 +250,34 @@ struct Stream {
   static constexpr int kSharers = PR ? kWaves : kWavesS;
   static constexpr int kDmaA = kDma * kWaves / kSharers;
   static constexpr int kDmaB = TG * NB * 4 / kSharers;
-  // VMEM instructions a wave issues after the DMAs of stage j's A rows, when it must have stage
-  // j: the B DMAs of the same iteration, then (kPWr - 1) full iterations.
-  static constexpr int kBudget = kDmaB + (kDmaA + kDmaB) * (kPWr - 1);
+  // VMEM instructions a wave issues after the later of stage j's DMAs, when it must have stage j.
+  // Stage j's A rows go out kPWr iterations ahead, followed in the same iteration by the B rows of
+  // stage j + kPXr - kPWr: when the B ring runs further ahead, those are later stages' rows (stage
+  // j's B rows went out earlier) and may still be in flight; with equal depths they are stage j's
+  // own B rows, and only the (kPWr - 1) later iterations may be.
+  static constexpr int kBudget = (kPXr > kPWr ? kDmaB : 0) + (kDmaA + kDmaB) * (kPWr - 1);
+  // The same count by walking the issue order (prologue and loop alike: iteration v issues A rows
+  // of stage v + kPWr, when >= 0, then B rows of stage v + kPXr): the instructions issued after
+  // the last DMA of stage j, up to the wait at the top of iteration j.  In-order completion makes
+  // "vmcnt <= kBudget" imply stage j has landed exactly when kBudget is at most this count.
+  static constexpr int issued_after(int j) {
+    int seq = 0, last = -1;
+    for (int v = -kPXr; v < j; ++v) {
+      if (v + kPWr >= 0) {
+        seq += kDmaA;
+        if (v + kPWr == j) last = seq;
+      }
+      seq += kDmaB;
+      if (v + kPXr == j) last = seq;
+    }
+    return seq - last;
+  }
+  static constexpr bool budget_holds() {
+    for (int j = 0; j < 2 * kUnr; ++j)
+      if (kBudget > issued_after(j)) return false;
+    return kBudget == issued_after(2 * kUnr);  // and no tighter than it need be in steady state
+  }
+  static_assert(budget_holds(), "the vmcnt budget must cover both DMA groups of the stage waited for");
   __amdgpu_buffer_rsrc_t ar, br, none;
   uint32_t voa[kDmaA], vob[kDmaB];
   uint32_t wave_off_a, wave_off_b, a_stage, b_stage;
@@ -305,16 +332,41 @@ struct Stream {
   }
 
   // acc <- the product over all nkb stages (after prologue()).  On return every DMA has landed
-  // and every wave is past its last operand read (the slots may be reused).
+  // and every wave is past its last operand read (the slots may be reused).  The DMA-only waves
+  // of the 64-row PR tile leave acc untouched.
   __device__ __forceinline__ void run(f32x16 (&acc)[kMBw][NB], int wave, int lane) {
     if constexpr (PR) {
-      if (issues)
+      if (!issues)
+        run_as<false>(acc, wave, lane);
+      else if constexpr (TG == kWaves)
         run_as<true>(acc, wave, lane);
       else
-        run_as<false>(acc, wave, lane);
+        run_dma_only();
     } else {
       run_as<true>(acc, wave, lane);
     }
+  }
+
+  // A wave that only feeds the rings: the same waits, barriers and DMAs per stage as run_as<true>,
+  // no LDS reads and no MFMAs.
+  __device__ __forceinline__ void run_dma_only() {
+    int j0 = 0;
+    do {
+#pragma unroll
+      for (int u = 0; u < kUnr; ++u) {
+        const int j = j0 + u;
+        if (j >= nkb) break;
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kBudget) & ~(15 << 8));
+        bare_barrier();
+        dma_rows<AUX_A, kDmaA>(ar, none, sl.w((u + kPWr) % kNWr) + wave_off_a, voa, phys(j + kPWr) * a_stage,
+                               j + kPWr < nkb);
+        dma_rows<AUX_B, kDmaB>(br, none, sl.x((u + kPXr) % kNXr) + wave_off_b, vob, phys(j + kPXr) * b_stage,
+                               j + kPXr < nkb);
+      }
+      j0 += kUnr;
+    } while (j0 < nkb);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0) & ~(15 << 8));
+    bare_barrier();
   }
 
   template <bool DMA>

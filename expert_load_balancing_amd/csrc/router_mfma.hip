@@ -15,8 +15,9 @@
 //   keeps the 256x256 fp32 logit tile in registers: each wave pair shares 64 tokens, and each
 //   wave of the pair holds 128 of the experts (8 accumulators of 32x32).  Batches of at most
 //   128 x 256 tokens (one 256-token tile per CU would leave CUs idle) take 128-token tiles
-//   instead: each wave pair 32 tokens.  Two waves per SIMD let one wave's LDS reads and
-//   selection run under the other's MFMAs.
+//   instead: each wave pair 32 tokens; batches of at most 64 x 256 take 64-token tiles, where
+//   waves 0-3 hold the product (two pairs of 32 tokens) and waves 4-7 only issue the DMAs.  Two
+//   waves per SIMD let one wave's LDS reads and selection run under the other's MFMAs.
 //   The contraction is written transposed, Z^T = W . X^T, so that the 32x32 MFMA output puts
 //   one token per lane column: a lane ends up holding 64 of its wave's 128 logits of each of
 //   its tokens, and the other 64 sit in lane ^ 32.  Top-K needs only a small LDS exchange: a
@@ -295,7 +296,9 @@ __device__ __forceinline__ void epilogue_split(const f32x16 (&acc)[kMB / 2][NB],
 
 // The ring slots fill the LDS; the epilogue reuses them once the ring drains.  The full tile
 // (NB = 2): tokens 3 x 32 KiB, weights 2 x 32 KiB.  The smaller tiles have shorter stages and
-// take deeper rings: 128 tokens 4 x 16 KiB + 3 x 32 KiB, 64 tokens 4 x 8 KiB + 4 x 32 KiB.
+// take deeper rings: 128 tokens 4 x 16 KiB + 3 x 32 KiB, 64 tokens 4 x 8 KiB + 4 x 32 KiB.  Each
+// kernel branch below declares exactly the slots its Ring names (checked at compile time: a
+// slot left out would be a null LDS address).
 template <int NB, int TG>
 struct Ring {
   static constexpr int NXR = NB == kNB ? kNX : 4;
@@ -326,7 +329,7 @@ __device__ __forceinline__ void router_body(Slots slots, Parks pk,
 
   // ---- operand streams: start the DMA ring (A = weights, B = this tile's tokens) ----
   const uint32_t row_bytes = (uint32_t)d * 2u;
-  Stream<kAuxCached, kAuxStream, RowsK, RowsK, NB, 2, TG == kWaves, TG, Ring<NB, TG>::NXR, Ring<NB, TG>::NWR> st;
+  Stream<kAuxCached, kAuxStream, RowsK, RowsK, NB, 2, true, TG, Ring<NB, TG>::NXR, Ring<NB, TG>::NWR> st;
   st.init(w, (uint32_t)n_experts * row_bytes, row_bytes, x + row0 * d, (uint32_t)rows * row_bytes, row_bytes,
           d / kBK, wave, lane, slots);
   // Rows a multiple of 4 KiB apart: every workgroup's rows share their low 12 address bits, so
@@ -351,8 +354,14 @@ __device__ __forceinline__ void router_body(Slots slots, Parks pk,
   }
   const float kscale = key_scale(mn, mx);  // identical in every wave: min and max are exact
   const float kbias = tid < n_experts ? key_bias(braw, mn, kscale) : 0.0f;
-  epilogue_split<K, FULL, EXTRA, NB>(acc, tid, wave, lane, row0, T, n_experts, normalize, kbias, kscale, pk, idx_out,
-                                     gates_out, logits, lse);
+  if (TG == kWaves || wave < kWaves) {
+    epilogue_split<K, FULL, EXTRA, NB>(acc, tid, wave, lane, row0, T, n_experts, normalize, kbias, kscale, pk,
+                                       idx_out, gates_out, logits, lse);
+  } else {
+    // The DMA-only waves of the 64-token tile hold no scores: they pass the epilogue's barriers.
+#pragma unroll
+    for (int i = 0; i < 1 + 2 * NB; ++i) bare_barrier();
+  }
 
   __attribute__((address_space(3))) int* const hist = (__attribute__((address_space(3))) int*)(pk.scratch + 1024);
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
@@ -368,7 +377,7 @@ __device__ __forceinline__ void router_body(Slots slots, Parks pk,
 }
 
 template <int K, bool FULL, bool EXTRA, int NB, int TG>
-__global__ __launch_bounds__(TG * 128) __attribute__((amdgpu_waves_per_eu(2, 2))) void router_mfma_kernel(
+__global__ __launch_bounds__(kWaves * 128) __attribute__((amdgpu_waves_per_eu(2, 2))) void router_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const float* __restrict__ bias, int64_t T, int d,
     int n_experts, int normalize, int32_t* __restrict__ idx_out, float* __restrict__ gates_out,
     int32_t* __restrict__ counts, float* __restrict__ logits, float* __restrict__ lse,
@@ -379,12 +388,14 @@ __global__ __launch_bounds__(TG * 128) __attribute__((amdgpu_waves_per_eu(2, 2))
   constexpr int XS = 32 * TG * NB * kRowB;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if constexpr (NB == kNB) {
+    static_assert(Ring<NB, TG>::NXR == 3 && Ring<NB, TG>::NWR == 2, "the slots declared here");
     __shared__ __attribute__((aligned(1024))) unsigned char xs0[XS], xs1[XS], xs2[XS], ws0[kSlot], ws1[kSlot];
     router_body<K, FULL, EXTRA, NB, TG>(
         Slots{xs0, xs1, xs2, ws0, ws1},
         make_parks(wave, ws1, xs0, xs0 + 16384, xs1, xs1 + 16384, xs2, xs2 + 16384, ws0, ws0 + 16384), x, w, bias, T, d,
         n_experts, normalize, idx_out, gates_out, counts, logits, lse, tile_loads, loads_stride);
   } else if constexpr (TG == kWaves) {
+    static_assert(Ring<NB, TG>::NXR == 4 && Ring<NB, TG>::NWR == 3, "the slots declared here");
     __shared__ __attribute__((aligned(1024))) unsigned char xs0[XS], xs1[XS], xs2[XS], xs3[XS];
     __shared__ __attribute__((aligned(1024))) unsigned char ws0[kSlot], ws1[kSlot], ws2[kSlot];
     router_body<K, FULL, EXTRA, NB, TG>(
@@ -392,6 +403,7 @@ __global__ __launch_bounds__(TG * 128) __attribute__((amdgpu_waves_per_eu(2, 2))
         make_parks(wave, xs2, ws0, ws0 + 16384, ws1, ws1 + 16384, ws2, ws2 + 16384, xs0, xs1), x, w, bias, T, d,
         n_experts, normalize, idx_out, gates_out, counts, logits, lse, tile_loads, loads_stride);
   } else {
+    static_assert(Ring<NB, TG>::NXR == 4 && Ring<NB, TG>::NWR == 4, "the slots declared here");
     __shared__ __attribute__((aligned(1024))) unsigned char xs0[XS], xs1[XS], xs2[XS], xs3[XS];
     __shared__ __attribute__((aligned(1024))) unsigned char ws0[kSlot], ws1[kSlot], ws2[kSlot], ws3[kSlot];
     router_body<K, FULL, EXTRA, NB, TG>(
@@ -408,10 +420,10 @@ hipError_t launch_kfn(const RouterArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)((a.T + kTok - 1) / kTok));
   int32_t* const loads = NB == kNB ? a.tile_loads : nullptr;
   if (a.logits != nullptr || a.lse != nullptr)
-    return launch_timed(router_mfma_kernel<K, FULL, true, NB, TG>, grid, dim3(TG * 128), 0, stream, nullptr, a.ev_stop,
+    return launch_timed(router_mfma_kernel<K, FULL, true, NB, TG>, grid, dim3(kWaves * 128), 0, stream, nullptr, a.ev_stop,
                         (const uint16_t*)a.x, (const uint16_t*)a.w, a.bias, a.T, a.d, a.n_experts, normalize, a.idx,
                         a.gates, a.counts, a.logits, a.lse, loads, a.loads_stride);
-  return launch_timed(router_mfma_kernel<K, FULL, false, NB, TG>, grid, dim3(TG * 128), 0, stream, nullptr, a.ev_stop,
+  return launch_timed(router_mfma_kernel<K, FULL, false, NB, TG>, grid, dim3(kWaves * 128), 0, stream, nullptr, a.ev_stop,
                       (const uint16_t*)a.x, (const uint16_t*)a.w, a.bias, a.T, a.d, a.n_experts, normalize, a.idx,
                       a.gates, a.counts, a.logits, a.lse, loads, a.loads_stride);
 }

@@ -45,22 +45,48 @@ __device__ __forceinline__ int wave_min(int v) {
   return v;
 }
 
-// Runs on the 64 lanes of the calling wave (lane = threadIdx.x & 63).
-__device__ __forceinline__ void balance_wave(const BalanceArgs& a) {
-  const int lane = threadIdx.x & 63;
-  const int n = a.n;
-  // Every load is issued up front: one memory round trip instead of one per dependent step.
-  const bool need_b = a.mode >= 0;
-  const bool need_m = a.mode >= 0 && a.mode != ELB_MODE_SIGN;
+// What one lane holds of the update's inputs: its experts lane + 64 r.
+struct BalanceIn {
   int c[kBalancePer];
   float b0[kBalancePer], m0[kBalancePer];
+};
+
+// Bias and momentum of the lane's experts (what the mode needs of them).
+__device__ __forceinline__ void balance_load_bm(const BalanceArgs& a, BalanceIn& in) {
+  const int lane = threadIdx.x & 63;
+  const bool need_b = a.mode >= 0;
+  const bool need_m = a.mode >= 0 && a.mode != ELB_MODE_SIGN;
 #pragma unroll
   for (int r = 0; r < kBalancePer; ++r) {
     const int e = lane + 64 * r;
-    c[r] = e < n ? a.counts[e] : 0;
-    b0[r] = need_b && e < n ? a.bias[e] : 0.0f;
-    m0[r] = need_m && e < n ? a.momentum[e] : 0.0f;
+    in.b0[r] = need_b && e < a.n ? a.bias[e] : 0.0f;
+    in.m0[r] = need_m && e < a.n ? a.momentum[e] : 0.0f;
   }
+}
+
+__device__ __forceinline__ void balance_apply(const BalanceArgs& a, const BalanceIn& in);
+
+// Runs on the 64 lanes of the calling wave (lane = threadIdx.x & 63).
+__device__ __forceinline__ void balance_wave(const BalanceArgs& a) {
+  const int lane = threadIdx.x & 63;
+  // Every load is issued up front: one memory round trip instead of one per dependent step.
+  BalanceIn in;
+#pragma unroll
+  for (int r = 0; r < kBalancePer; ++r) {
+    const int e = lane + 64 * r;
+    in.c[r] = e < a.n ? a.counts[e] : 0;
+  }
+  balance_load_bm(a, in);
+  balance_apply(a, in);
+}
+
+// The update from the lane's inputs; with a.clear, zeroes the lane's entries of a.counts.
+__device__ __forceinline__ void balance_apply(const BalanceArgs& a, const BalanceIn& in) {
+  const int lane = threadIdx.x & 63;
+  const int n = a.n;
+  const int* const c = in.c;
+  const float* const b0 = in.b0;
+  const float* const m0 = in.m0;
   long long lsum = 0;
   int lmax = -2147483647 - 1, lmin = 2147483647;
 #pragma unroll
@@ -71,7 +97,7 @@ __device__ __forceinline__ void balance_wave(const BalanceArgs& a) {
       lmin = min(lmin, c[r]);
     }
   }
-  if (a.clear) {  // each lane clears exactly the entries it read
+  if (a.clear) {  // each lane clears exactly its own entries
 #pragma unroll
     for (int r = 0; r < kBalancePer; ++r) {
       const int e = lane + 64 * r;

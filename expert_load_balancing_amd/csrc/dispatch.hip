@@ -9,22 +9,40 @@
 //
 // A tile is 256 tokens, all K slots of each: 256 K consecutive flat entries.  Workspace:
 //   loads  [n_experts][stride] int32: entries of tile b routed to expert e, then (after the
-//          scan) the number of such entries in tiles before b;
-//   totals [n_experts] int32.
-//  1. loads:   one workgroup per tile, LDS histogram.  Skipped when the MFMA router kernel
-//              already stored its own tile histogram in the table.
-//  2. scan:    one wave per expert scans its row in place and writes the expert's total (and,
-//              in a routed step, adds it into the step's expert loads: the router kernel then
-//              leaves `counts` alone, which spares 256 contended global atomics per tile).
-//  3. scatter: one workgroup per tile, one pass.  With a bias update requested, one more
-//              workgroup runs it (balance_wave.hpp): the update reads only `counts`, which are
-//              final once the router kernel is done, and its few microseconds of dependent
-//              memory round trips hide behind the scatter's (the scan is shorter).  Each block scans the expert totals itself
-//              (a few hundred cycles) for the bucket starts.  Entry c * 256 + tid of the tile
-//              goes to thread tid; each 64-entry run ("virtual wave" v = c * 4 + wave, in
-//              ascending j) ranks its lanes by expert with 8 ballots (one per bit of e), the
-//              last lane of each expert stores the run's count, and one in-place scan per
-//              expert over the runs turns those counts into run offsets.
+//          scan) kScanned | the number of such entries in tiles before b;
+//   totals [n_experts] int32: kScanned | the expert's total once scanned, reset to 0 by
+//          whichever kernel fills the table.
+//  1. loads: one workgroup per tile, LDS histogram.  Skipped when the MFMA router kernel
+//     already stored its own tile histogram in the table (and reset the totals).
+//  2. one launch with three kinds of workgroup, in this block order:
+//     scan    block e < n_experts scans row e in place and writes the expert's total (and, in a
+//             routed step without an update, sets or adds it into the step's expert loads: the
+//             router kernel then leaves `counts` alone, which spares 256 contended global
+//             atomics per tile).  Every scanned entry and total carries the flag bit kScanned
+//             (all of them are below 2^31), so each one shows by itself whether it is final;
+//     scatter one block per tile (the tiles of each XCD contiguous).  It ranks its entries first
+//             (independent of the scan): entry c * 256 + tid of the tile goes to thread tid;
+//             each 64-entry run ("virtual wave" v = c * 4 + wave, in ascending j) ranks its lanes
+//             by expert with 8 ballots (one per bit of e), and the last lane of each expert
+//             stores the run's count.  Then each
+//             thread polls just the two words it needs, its expert's total and the entry of this
+//             tile, until both carry the flag (a value is published by the one store that writes
+//             it: no counter, no store-completion wait).  Each block scans the expert totals
+//             itself (a few hundred cycles) for the bucket starts, and one in-place scan per
+//             expert over the runs turns the run counts into run offsets;
+//     update  with a bias update requested, one last block: its wave polls the totals the same
+//             way, forms the step's loads (adding the earlier ones with ELB_ACCUMULATE_COUNTS),
+//             stores them in `counts` unless ELB_CLEAR_COUNTS zeroes them, and runs the update
+//             on them (balance_wave.hpp).
+//     Only blocks after the scan blocks ever wait, and scan blocks never wait: blocks are
+//     dispatched in index order, so every waited-for block has been dispatched and finishes.  The
+//     wait is also bounded (about a second), so no fault elsewhere can turn it into a hang.
+//     Visibility across the XCDs' separate L2 caches: the scan's results are written and read
+//     with agent-scope atomic stores and loads (coherent accesses that go past the XCD's L2).
+//     A count of finished rows with a release / acquire pair around it would also work, but the
+//     release and acquire write back and invalidate whole L2 caches, once per block, and a
+//     counter that every block polls while the scan blocks add to it holds those adds up: that
+//     form made this launch slower than the separate scan kernel it replaces.
 #include "balance_wave.hpp"
 #include "device_common.hpp"
 #include "elb_kernels.h"
@@ -65,6 +83,8 @@ __global__ __launch_bounds__(kThreads) void dispatch_loads_kernel(const int32_t*
                                                                   int32_t* __restrict__ loads) {
   __shared__ int hist[kMaxExperts];
   hist[threadIdx.x] = 0;
+  // Filling the table also resets the totals the scan will flag.
+  if (blockIdx.x == 0 && (int)threadIdx.x < n_experts) loads[stride * n_experts + threadIdx.x] = 0;
   __syncthreads();
   const int64_t lo = (int64_t)blockIdx.x * kDispatchTile * k;
   const int64_t hi = lo + (int64_t)kDispatchTile * k < total ? lo + (int64_t)kDispatchTile * k : total;
@@ -76,16 +96,19 @@ __global__ __launch_bounds__(kThreads) void dispatch_loads_kernel(const int32_t*
   if ((int)threadIdx.x < n_experts) loads[(int64_t)threadIdx.x * stride + blockIdx.x] = hist[threadIdx.x];
 }
 
-// Block e < n_experts scans row e.
-__global__ __launch_bounds__(64) void dispatch_scan_kernel(int32_t* __restrict__ loads, int64_t n_tiles,
-                                                           int64_t stride, int n_experts,
-                                                           int32_t* __restrict__ totals,
-                                                           int32_t* __restrict__ counts, int accumulate) {
-  const int lane = threadIdx.x;
-  int32_t* const row = loads + (int64_t)blockIdx.x * stride;
+constexpr int kSpinLimit = 1 << 22;  // polls of one word, 512 cycles apart: about a second
+constexpr int kScanned = int(0x80000000u);  // flag bit of a scanned table entry or total
+
+// Scan block: row e of the loads table, in chunks of 4 entries per thread.
+__device__ __forceinline__ void scan_row(int e, int32_t* __restrict__ loads, int64_t n_tiles, int64_t stride,
+                                         int32_t* __restrict__ totals, int32_t* __restrict__ counts, int accumulate) {
+  __shared__ int wsum[kWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int32_t* const row = loads + (int64_t)e * stride;
+  auto put = [](int32_t* p, int v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
   int carry = 0;
-  for (int64_t c0 = 0; c0 < n_tiles; c0 += 256) {
-    const int64_t t0 = c0 + 4 * lane;  // stride % 4 == 0: t0 < stride covers t0 .. t0 + 3
+  for (int64_t c0 = 0; c0 < n_tiles; c0 += 4 * kThreads) {
+    const int64_t t0 = c0 + 4 * tid;  // stride % 4 == 0: t0 < stride covers t0 .. t0 + 3
     i32x4 v = {0, 0, 0, 0};
     if (t0 < stride) v = *reinterpret_cast<const i32x4*>(row + t0);
 #pragma unroll
@@ -93,36 +116,93 @@ __global__ __launch_bounds__(64) void dispatch_scan_kernel(int32_t* __restrict__
       if (t0 + q >= n_tiles) v[q] = 0;  // padding columns hold stale workspace
     const int local = v[0] + v[1] + v[2] + v[3];
     const int incl = wave_inclusive_scan(local);
-    const int excl = carry + incl - local;
-    if (t0 < stride)
-      *reinterpret_cast<i32x4*>(row + t0) = i32x4{excl, excl + v[0], excl + v[0] + v[1], excl + v[0] + v[1] + v[2]};
-    carry += __shfl(incl, 63);
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int before = 0, chunk = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      before += w < wave ? wsum[w] : 0;
+      chunk += wsum[w];
+    }
+    const int excl = carry + before + incl - local;
+    if (t0 < stride) {
+      put(row + t0, kScanned | excl);
+      put(row + t0 + 1, kScanned | (excl + v[0]));
+      put(row + t0 + 2, kScanned | (excl + v[0] + v[1]));
+      put(row + t0 + 3, kScanned | (excl + v[0] + v[1] + v[2]));
+    }
+    carry += chunk;
+    __syncthreads();  // wsum is rewritten by the next chunk
   }
-  if (lane == 0) {
-    totals[blockIdx.x] = carry;
-    if (counts != nullptr) counts[blockIdx.x] = (accumulate ? counts[blockIdx.x] : 0) + carry;
+  if (tid == 0) {
+    put(totals + e, kScanned | carry);
+    if (counts != nullptr) counts[e] = (accumulate ? counts[e] : 0) + carry;
   }
 }
 
+// A scanned word: its first (coherent, agent-scope atomic) load is issued with the others the
+// caller needs, then finish() polls it (~0.25 us apart) until it carries kScanned.
+__device__ __forceinline__ int load_scanned(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int finish_scanned(const int32_t* p, int v) {
+  for (int spins = 0; (v & kScanned) == 0 && spins < kSpinLimit; ++spins) {
+    __builtin_amdgcn_s_sleep(8);
+    v = load_scanned(p);
+  }
+  return v & ~kScanned;
+}
+
 template <int K>
-__global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(const int32_t* __restrict__ idx, int64_t total,
-                                                                    int n_experts, int64_t stride,
-                                                                    const int32_t* __restrict__ loads,
-                                                                    const int32_t* __restrict__ totals,
-                                                                    int32_t* __restrict__ offsets,
-                                                                    int32_t* __restrict__ perm,
-                                                                    int32_t* __restrict__ inv, BalanceArgs update) {
-  if ((int64_t)blockIdx.x == (total + kDispatchTile * K - 1) / (kDispatchTile * K)) {
-    // The block after the last tile (launched only with an update): the bias update, one wave.
-    if (threadIdx.x < 64) balance_wave(update);
+__global__ __launch_bounds__(kThreads) void dispatch_kernel(const int32_t* __restrict__ idx, int64_t total,
+                                                            int n_experts, int64_t n_tiles, int64_t stride,
+                                                            int32_t* __restrict__ loads,
+                                                            int32_t* __restrict__ totals,
+                                                            int32_t* __restrict__ counts, int accumulate,
+                                                            int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ perm,
+                                                            int32_t* __restrict__ inv, BalanceArgs update) {
+  if ((int)blockIdx.x < n_experts) {
+    // With an update, the update block sets the counts (it must store them before it clears them).
+    scan_row((int)blockIdx.x, loads, n_tiles, stride, totals, update.counts != nullptr ? nullptr : counts, accumulate);
     return;
   }
+  // Tile blocks: padded to a multiple of 8, and those that land on one XCD (blocks go to the 8
+  // XCDs in turn) take one contiguous range of tiles.  Neighbouring tiles write neighbouring
+  // pieces (about K entries each) of every expert's bucket, so the partial lines of perm meet in
+  // one L2 and go to memory whole, instead of piecewise from every XCD.
+  const int64_t n_pad = (n_tiles + 7) / 8 * 8;
+  const int64_t tb = (int64_t)blockIdx.x - n_experts;
+  if (tb == n_pad) {
+    // The block after the tile blocks (launched only with an update): the bias update, one wave.
+    if (threadIdx.x < 64) {
+      BalanceIn in;
+      balance_load_bm(update, in);  // issued before the wait
+      int t[kBalancePer];
+#pragma unroll
+      for (int r = 0; r < kBalancePer; ++r) {
+        const int e = (int)threadIdx.x + 64 * r;
+        t[r] = e < n_experts ? load_scanned(totals + e) : kScanned;
+        in.c[r] = e < n_experts && accumulate ? update.counts[e] : 0;
+      }
+#pragma unroll
+      for (int r = 0; r < kBalancePer; ++r) {
+        const int e = (int)threadIdx.x + 64 * r;
+        in.c[r] += finish_scanned(totals + e, t[r]);
+        if (e < n_experts && !update.clear) update.counts[e] = in.c[r];
+      }
+      balance_apply(update, in);
+    }
+    return;
+  }
+  const int64_t tile = (tb % 8) * (n_pad / 8) + tb / 8;
+  if (tile >= n_tiles) return;
   __shared__ int wsum[kWaves];
   __shared__ int vcnt[K * kWaves][kMaxExperts];  // per virtual wave: count, then start
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int64_t lo = (int64_t)blockIdx.x * (kDispatchTile * K);
+  const int64_t lo = tile * (kDispatchTile * K);
 
   int e[K];
 #pragma unroll
@@ -131,21 +211,9 @@ __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(const int32_
     const int raw = j < total ? idx[j] : -1;
     e[c] = (unsigned)raw < (unsigned)n_experts ? raw : -1;  // out-of-range ids are dropped
   }
-  const int tot = tid < n_experts ? totals[tid] : 0;
-  const int before = tid < n_experts ? loads[(int64_t)tid * stride + blockIdx.x] : 0;
 #pragma unroll
   for (int v = 0; v < K * kWaves; ++v) vcnt[v][tid] = 0;
-
-  // Bucket start of expert tid: exclusive scan of the totals.
-  const int incl = wave_inclusive_scan(tot);
-  if (lane == 63) wsum[wave] = incl;
   __syncthreads();
-  int start = incl - tot;
-  for (int w = 0; w < wave; ++w) start += wsum[w];
-  if (blockIdx.x == 0) {
-    if (tid < n_experts) offsets[tid] = start;
-    if (tid == 0) offsets[n_experts] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-  }
 
   // Rank inside each 64-entry run: lanes below with the same expert.
   const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
@@ -164,7 +232,27 @@ __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(const int32_
     const int cnt = __popcll(peers);
     if (valid && rank[c] == cnt - 1) vcnt[c * kWaves + wave][key] = cnt;  // the last peer in lane order
   }
+
+  // The tile's offsets need the scan: totals and this tile's column of the scanned table.
+  const int32_t* const at = loads + (int64_t)tid * stride + tile;
+  int tot = 0, before = 0;
+  if (tid < n_experts) {
+    tot = load_scanned(totals + tid);
+    before = load_scanned(at);
+    tot = finish_scanned(totals + tid, tot);
+    before = finish_scanned(at, before);
+  }
+
+  // Bucket start of expert tid: exclusive scan of the totals.
+  const int incl = wave_inclusive_scan(tot);
+  if (lane == 63) wsum[wave] = incl;
   __syncthreads();
+  int start = incl - tot;
+  for (int w = 0; w < wave; ++w) start += wsum[w];
+  if (tile == 0) {
+    if (tid < n_experts) offsets[tid] = start;
+    if (tid == 0) offsets[n_experts] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  }
   // Run offsets of expert tid: its bucket start, plus earlier tiles, plus earlier runs.
   if (tid < n_experts) {
     int run = start + before;
@@ -188,13 +276,15 @@ __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(const int32_
 }
 
 template <int K>
-hipError_t launch_scatter(const int32_t* idx, int64_t total, int n_experts, const DispatchGeom& g,
-                          const int32_t* loads, const int32_t* totals, int32_t* offsets, int32_t* perm, int32_t* inv,
-                          const BalanceArgs* update, hipStream_t stream, hipEvent_t ev_stop) {
+hipError_t launch_dispatch_k(const int32_t* idx, int64_t total, int n_experts, const DispatchGeom& g, int32_t* loads,
+                             int32_t* totals, int32_t* counts, bool accumulate, int32_t* offsets,
+                             int32_t* perm, int32_t* inv, const BalanceArgs* update, hipStream_t stream,
+                             hipEvent_t ev_stop) {
   const BalanceArgs none{};
-  return launch_timed(dispatch_scatter_kernel<K>, dim3((unsigned)(g.n_tiles + (update != nullptr ? 1 : 0))),
-                      dim3(kThreads), 0, stream, nullptr, ev_stop, idx, total, n_experts, g.stride, loads, totals,
-                      offsets, perm, inv, update != nullptr ? *update : none);
+  const int64_t blocks = n_experts + (g.n_tiles + 7) / 8 * 8 + (update != nullptr ? 1 : 0);
+  return launch_timed(dispatch_kernel<K>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, nullptr, ev_stop, idx,
+                      total, n_experts, g.n_tiles, g.stride, loads, totals, counts, accumulate ? 1 : 0, offsets,
+                      perm, inv, update != nullptr ? *update : none);
 }
 
 }  // namespace
@@ -250,26 +340,27 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t T, int k, int n_experts, 
   const int64_t total = T * k;
   int32_t* loads = static_cast<int32_t*>(workspace);
   int32_t* totals = loads + g.stride * n_experts;
-  hipError_t err = hipSuccess;
   if (!loads_ready) {
-    err = launch(dispatch_loads_kernel, dim3((unsigned)g.n_tiles), dim3(kThreads), 0, stream, idx, total, k,
-                 n_experts, g.stride, loads);
+    const hipError_t err = launch(dispatch_loads_kernel, dim3((unsigned)g.n_tiles), dim3(kThreads), 0, stream, idx,
+                                  total, k, n_experts, g.stride, loads);
     if (err != hipSuccess) return err;
   }
-  err = launch(dispatch_scan_kernel, dim3((unsigned)n_experts), dim3(64), 0, stream, loads, g.n_tiles, g.stride,
-               n_experts, totals, counts, accumulate ? 1 : 0);
-  if (err != hipSuccess) return err;
-  const int32_t* cl = loads;
-  const int32_t* ct = totals;
   switch (k) {
-    case 1: return launch_scatter<1>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, update, stream, ev_stop);
-    case 2: return launch_scatter<2>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, update, stream, ev_stop);
-    case 3: return launch_scatter<3>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, update, stream, ev_stop);
-    case 4: return launch_scatter<4>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, update, stream, ev_stop);
-    case 5: return launch_scatter<5>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, update, stream, ev_stop);
-    case 6: return launch_scatter<6>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, update, stream, ev_stop);
-    case 7: return launch_scatter<7>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, update, stream, ev_stop);
-    default: return launch_scatter<8>(idx, total, n_experts, g, cl, ct, offsets, perm, inv, update, stream, ev_stop);
+#define ELB_DISPATCH_K(KK) \
+  case KK:                 \
+    return launch_dispatch_k<KK>(idx, total, n_experts, g, loads, totals, counts, accumulate, offsets, perm, inv, \
+                                 update, stream, ev_stop);
+    ELB_DISPATCH_K(1)
+    ELB_DISPATCH_K(2)
+    ELB_DISPATCH_K(3)
+    ELB_DISPATCH_K(4)
+    ELB_DISPATCH_K(5)
+    ELB_DISPATCH_K(6)
+    ELB_DISPATCH_K(7)
+#undef ELB_DISPATCH_K
+    default:
+      return launch_dispatch_k<8>(idx, total, n_experts, g, loads, totals, counts, accumulate, offsets, perm,
+                                  inv, update, stream, ev_stop);
   }
 }
 

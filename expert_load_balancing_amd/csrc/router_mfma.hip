@@ -374,6 +374,9 @@ __device__ __forceinline__ void router_body(Slots slots, Parks pk,
     // passes no table with the half tile).
     if (NB == kNB && tile_loads != nullptr) tile_loads[(int64_t)tid * loads_stride + blockIdx.x] = n;
   }
+  // Filling the table also resets the totals the dispatch scan will flag.
+  if (NB == kNB && tile_loads != nullptr && blockIdx.x == 0 && tid < n_experts)
+    tile_loads[loads_stride * n_experts + tid] = 0;
 }
 
 template <int K, bool FULL, bool EXTRA, int NB, int TG>

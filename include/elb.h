@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define ELB_VERSION 10700 /* major * 10000 + minor * 100 + patch */
+#define ELB_VERSION 10800 /* major * 10000 + minor * 100 + patch */
 
 typedef struct ihipStream_t* elb_stream_t; /* hipStream_t; NULL = default stream */
 
@@ -177,15 +177,15 @@ elb_status elb_smebu_update(int32_t* counts, int32_t n_experts, elb_balance_para
                             elb_stream_t stream);
 
 /*
- * One routed step in three kernels: elb_router_forward, then elb_router_dispatch of its
- * topk_idx, then (when `update` is non-zero) elb_smebu_update from `counts`.  Each field
- * means what the argument of the same name means in those calls, and the same checks apply.
- * Compared with the three calls in a row, the router kernel stores each 256-token tile's loads
- * in the dispatch workspace (the dispatch does not count them again; bf16 inputs with
- * d % 64 == 0 only, else a counting pass runs), the dispatch's scan over those tile loads
- * writes (with ELB_ACCUMULATE_COUNTS: adds) `counts` in place of the router kernel's per-tile
- * atomics, and the bias update runs inside the dispatch's scatter launch.  The counts are the
- * same integers either way.  The update sees `counts` after this batch's loads were added, and changes
+ * One routed step: elb_router_forward, then elb_router_dispatch of its topk_idx, then (when
+ * `update` is non-zero) elb_smebu_update from `counts`.  Each field means what the argument of
+ * the same name means in those calls, and the same checks apply.  Compared with the three
+ * calls in a row, the router kernel stores each 256-token tile's loads in the dispatch
+ * workspace (the dispatch does not count them again; bf16 inputs with d % 64 == 0 only, else
+ * a counting pass runs), the dispatch's scan over those tile loads writes (with
+ * ELB_ACCUMULATE_COUNTS: adds) `counts` in place of the router kernel's per-tile atomics, and
+ * the bias update runs inside the dispatch's launch: two kernels in all (router, dispatch).
+ * The counts are the same integers either way.  The update sees `counts` after this batch's loads were added, and changes
  * `bias` only after the router kernel has read it, so the next step routes with the new bias.
  * A training loop with one batch per optimizer step sets ELB_ACCUMULATE_COUNTS and
  * ELB_CLEAR_COUNTS and never resets `counts` itself (they must start at zero).

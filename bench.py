@@ -350,18 +350,23 @@ def time_steps(s: Setup, steps: int, warmup: int, stream) -> tuple[float, object
 def step_median(s: Setup, reps: int) -> dict:
     """Each of `reps` steps bracketed on its own: from the end of an empty kernel launched just
     before the router kernel to the end of the step's last kernel (fence-free events bound to
-    the kernels).  Each interval therefore includes one dispatch gap, a few microseconds."""
+    the kernels).  Each interval therefore includes one dispatch gap, a few microseconds.  A third
+    event takes the router kernel's own end, which splits each step into the router kernel (with
+    that gap) and what follows it: the dispatch launch, with the bias update inside it."""
     import torch
 
-    ev = [(TimingEvent(), TimingEvent()) for _ in range(reps)]
-    for a, b in ev:
-        s.step.set_timing(a, None, b)
+    ev = [(TimingEvent(), TimingEvent(), TimingEvent()) for _ in range(reps)]
+    for a, r, b in ev:
+        s.step.set_timing(a, r, b)
         s()
     s.step.set_timing()
     torch.cuda.synchronize()
-    us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    us = sorted(a.elapsed_time(b) * 1e3 for a, r, b in ev)
+    router = sorted(a.elapsed_time(r) * 1e3 for a, r, b in ev)
+    after = sorted(r.elapsed_time(b) * 1e3 for a, r, b in ev)
     return {"median": round(statistics.median(us), 2), "min": round(us[0], 2), "max": round(us[-1], 2),
-            "reps": reps}
+            "reps": reps, "router_median": round(statistics.median(router), 2),
+            "after_router_median": round(statistics.median(after), 2), "after_router_min": round(after[0], 2)}
 
 
 def router_back_to_back(elb, s: Setup, launches: int) -> float:
@@ -406,7 +411,8 @@ def bench_config(elb, key: str, dev, stream, steps: int, launches: int) -> dict:
     ms, _ = time_steps(s, steps, max(5, steps // 5), stream)
     med = step_median(s, max(50, steps))
     res = {"workload": wl.label, "routed_tokens_per_s": round(wl.T / (ms * 1e-3), 1), "step_us": round(ms * 1e3, 2),
-           "step_us_median": med["median"]}
+           "step_us_median": med["median"], "router_in_step_us_median": med["router_median"],
+           "after_router_us_median": med["after_router_median"]}
     if wl.dtype == "bf16":
         r = roofline_of(wl, router_back_to_back(elb, s, launches))
         res.update({"router_us": r["kernel_us"], "router_frac": r["frac"], "router_GBps": r["achieved"],
@@ -566,6 +572,9 @@ def main() -> int:
                      "mfma_frac": r["mfma_frac"]},
         "breakdown_us": {"step": round(ms * 1e3, 2), "step_median": med["median"], "step_min": med["min"],
                          "step_max": med["max"], "step_median_reps": med["reps"],
+                         "router_in_step_median": med["router_median"],
+                         "after_router_median": med["after_router_median"],
+                         "after_router_min": med["after_router_min"],
                          "router_back_to_back": r["kernel_us"]},
         "dispatch": dispatch,
         "maxvio_last": float(mv.cpu()[0]),

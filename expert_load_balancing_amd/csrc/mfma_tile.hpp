@@ -242,7 +242,7 @@ struct Stream {
   static_assert(ES == 1 || (ES == 2 && (PR || (LA::kReads == 1 && LB::kReads == 1))), "the 8-wave DMA split");
   static_assert(!PR || (ES == 2 && (TG == kWaves || TG == 2)), "DMA-issuing waves need a second wave per SIMD");
   static_assert(TG == kWaves || (TG == 2 && ES == 2 && NB == 1 && LA::kReads == 1 && LB::kReads == 1),
-                "the 64-row B tile: 4 waves, rows-contiguous-in-k");
+                "the 64-row B tile: 4 multiplying waves, rows-contiguous-in-k");
   static constexpr int kWavesS = TG * ES;
   static constexpr int kMBw = kMB / ES;  // A blocks per wave
   // Waves that issue the DMAs, and DMA instructions per issuing wave per stage (1 KiB each): A's

@@ -95,7 +95,7 @@ __device__ __forceinline__ float sigmoid_fast(float z) {
 
 // Epilogue of the 8-wave tile.  Wave w holds experts 128 eh .. + 127 (eh = w % 2) of
 // tokens 32 NB tq .. (tq = w / 2); a lane holds 64 of them for its token, lane ^ 32 the other 64.
-// Per 32-token block: every wave selects its K best (same keys as the 4-wave epilogue, a
+// Per 32-token block: every wave selects its K best (keys as described at the top, a
 // lane-local slot in the low bits, re-keyed with 255 - expert before the merges), parks its
 // scores, and leaves its K keys (and, with EXTRA, its log-sum-exp partial) in LDS; after a
 // barrier one wave of each pair (eh = block parity) merges the partner's K keys and writes the

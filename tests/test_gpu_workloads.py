@@ -92,9 +92,10 @@ def test_full_size_workload(key):
 
 @pytest.mark.parametrize("key", ["tiny", "sign", "large", "stress"])
 def test_full_size_workload_fused_step(key):
-    """The same workloads through elb_route_step (one call, three or four kernels): outputs equal
-    the separate calls' bit for bit -- the generic kernel plus a counting pass for the fp32
-    workload, the dispatch scan over 1024 tiles for the stress workload."""
+    """The same workloads through elb_route_step (one call: the router kernel, then the dispatch
+    launch, with a counting pass between them where the router's tiles are not the dispatch's):
+    outputs equal the separate calls' bit for bit -- the generic kernel plus a counting pass for
+    the fp32 workload, the dispatch's scan blocks over 1024 tiles for the stress workload."""
     wl = datagen.WORKLOADS[key]
     log(f"fused step on {wl.label}")
     x, w = datagen.tokens(wl), datagen.router_weight(wl)

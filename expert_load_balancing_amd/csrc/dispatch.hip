@@ -20,6 +20,10 @@
 //             router kernel then leaves `counts` alone, which spares 256 contended global
 //             atomics per tile).  Every scanned entry and total carries the flag bit kScanned
 //             (all of them are below 2^31), so each one shows by itself whether it is final;
+//     update  with a bias update requested, one block: its wave polls the totals the same way
+//             as the scatter blocks below, forms the step's loads (adding the earlier ones with
+//             ELB_ACCUMULATE_COUNTS), stores them in `counts` unless ELB_CLEAR_COUNTS zeroes them,
+//             and runs the update on them (balance_wave.hpp);
 //     scatter one block per tile (the tiles of each XCD contiguous).  It ranks its entries first
 //             (independent of the scan): entry c * 256 + tid of the tile goes to thread tid;
 //             each 64-entry run ("virtual wave" v = c * 4 + wave, in ascending j) ranks its lanes
@@ -29,11 +33,7 @@
 //             tile, until both carry the flag (a value is published by the one store that writes
 //             it: no counter, no store-completion wait).  Each block scans the expert totals
 //             itself (a few hundred cycles) for the bucket starts, and one in-place scan per
-//             expert over the runs turns the run counts into run offsets;
-//     update  with a bias update requested, one last block: its wave polls the totals the same
-//             way, forms the step's loads (adding the earlier ones with ELB_ACCUMULATE_COUNTS),
-//             stores them in `counts` unless ELB_CLEAR_COUNTS zeroes them, and runs the update
-//             on them (balance_wave.hpp).
+//             expert over the runs turns the run counts into run offsets.
 //     Only blocks after the scan blocks ever wait, and scan blocks never wait: blocks are
 //     dispatched in index order, so every waited-for block has been dispatched and finishes.  The
 //     wait is also bounded (about a second), so no fault elsewhere can turn it into a hang.
@@ -167,14 +167,12 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(const int32_t* __res
     scan_row((int)blockIdx.x, loads, n_tiles, stride, totals, update.counts != nullptr ? nullptr : counts, accumulate);
     return;
   }
-  // Tile blocks: padded to a multiple of 8, and those that land on one XCD (blocks go to the 8
-  // XCDs in turn) take one contiguous range of tiles.  Neighbouring tiles write neighbouring
-  // pieces (about K entries each) of every expert's bucket, so the partial lines of perm meet in
-  // one L2 and go to memory whole, instead of piecewise from every XCD.
-  const int64_t n_pad = (n_tiles + 7) / 8 * 8;
-  const int64_t tb = (int64_t)blockIdx.x - n_experts;
-  if (tb == n_pad) {
-    // The block after the tile blocks (launched only with an update): the bias update, one wave.
+  // With an update, the block right after the scan blocks runs it: dispatched ahead of the tile
+  // blocks, it starts waiting for the totals as soon as the scans do (placed after the tile
+  // blocks it started ~0.5-1 us later at 1024 tiles).
+  const bool has_update = update.counts != nullptr;
+  if (has_update && (int)blockIdx.x == n_experts) {
+    // The bias update, one wave.
     if (threadIdx.x < 64) {
       BalanceIn in;
       balance_load_bm(update, in);  // issued before the wait
@@ -195,6 +193,12 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(const int32_t* __res
     }
     return;
   }
+  // Tile blocks: padded to a multiple of 8, and those that land on one XCD (blocks go to the 8
+  // XCDs in turn) take one contiguous range of tiles.  Neighbouring tiles write neighbouring
+  // pieces (about K entries each) of every expert's bucket, so the partial lines of perm meet in
+  // one L2 and go to memory whole, instead of piecewise from every XCD.
+  const int64_t n_pad = (n_tiles + 7) / 8 * 8;
+  const int64_t tb = (int64_t)blockIdx.x - n_experts - (has_update ? 1 : 0);
   const int64_t tile = (tb % 8) * (n_pad / 8) + tb / 8;
   if (tile >= n_tiles) return;
   __shared__ int wsum[kWaves];

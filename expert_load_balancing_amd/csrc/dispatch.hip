@@ -273,6 +273,9 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(const int32_t* __res
     if (e[c] >= 0) {
       const int64_t j = lo + c * kThreads + tid;
       const int pos = vcnt[c * kWaves + wave][e[c]] + rank[c];
+      // Always in range once the scan has been seen; only a wait that ran out (kSpinLimit)
+      // could leave pos outside [0, total), and then the store is dropped, never misplaced.
+      if ((uint32_t)pos >= (uint32_t)total) continue;
       perm[pos] = (int32_t)j;
       if (inv != nullptr) inv[j] = pos;
     }

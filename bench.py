@@ -88,10 +88,13 @@ class TimingEvent:
             TimingEvent._hip.hipEventDestroy(ctypes.c_void_p(self.cuda_event))
 
 
-def router_kernel_name(T: int, n_e: int, k: int) -> str:
-    """The MFMA router instantiation a forward of T tokens runs, as the profiler names it:
-    <K, all 256 experts, no logits/lse copy, 32-token blocks per wave pair, waves / 2> with the
-    256-token tile above 128 x 256 tokens, the 128-token tile above 64 x 256, else the 64-token."""
+def router_kernel_name(T: int, n_e: int, k: int, dtype: str = "bf16") -> str:
+    """The router instantiation a forward of T tokens runs, as the profiler names it.  bf16: the
+    MFMA kernel <K, all 256 experts, no logits/lse copy, 32-token blocks per wave pair, waves / 2>
+    with the 256-token tile above 128 x 256 tokens, the 128-token tile above 64 x 256, else the
+    64-token; fp32: the generic kernel <float, token subsets (4 up to 64 experts, 2 up to 128)>."""
+    if dtype != "bf16":
+        return f"router_generic_kernel<float, {4 if n_e <= 64 else 2 if n_e <= 128 else 1}>"
     nb, tg = (2, 4) if T > 128 * 256 else (1, 4) if T > 64 * 256 else (1, 2)
     return f"router_mfma_kernel<{k}, {'true' if n_e == 256 else 'false'}, false, {nb}, {tg}>"
 
@@ -567,7 +570,7 @@ def main() -> int:
                    "dispatch": wl.dispatch, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": r["achieved"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": r["frac"], "traffic": None if traffic is None else round(traffic),
-                     "kernel": router_kernel_name(T, n_e, k), "alg_bytes_per_launch": r["alg_bytes_per_launch"],
+                     "kernel": router_kernel_name(T, n_e, k, wl.dtype), "alg_bytes_per_launch": r["alg_bytes_per_launch"],
                      "launches_timed": n_solo, "kernel_us": r["kernel_us"], "mfma_tflops": r["mfma_tflops"],
                      "mfma_frac": r["mfma_frac"]},
         "breakdown_us": {"step": round(ms * 1e3, 2), "step_median": med["median"], "step_min": med["min"],

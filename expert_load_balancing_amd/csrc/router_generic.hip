@@ -9,9 +9,10 @@
 //   z = u_t . e_i (fp32 FMA, ascending k), s = 1 / (1 + exp(-z)), q = s + b_i;
 //   the K largest q are chosen one at a time (ties to the lower index), gates come from s.
 //
-// Layout: a workgroup of 256 threads handles 8 tokens at a time, thread i owning expert i.
-// The 8 token rows are staged through LDS in chunks of 256 elements; each thread streams its
-// own weight row.  Selection runs one token per wave-pass with a shuffle arg-max.
+// Layout: a workgroup of 256 threads handles 8 tokens at a time, thread i owning expert i (with
+// at most 64 or 128 experts, the waves split the 8 tokens between them, each thread then owning
+// expert i mod 64 or 128).  The 8 token rows are staged through LDS in chunks of 256 elements;
+// each thread streams its own weight row.  Selection runs one token per wave-pass with a shuffle arg-max.
 #include "device_common.hpp"
 #include "elb_kernels.h"
 
@@ -27,7 +28,40 @@ constexpr int kChunk = 256; // row elements staged per pass
 __device__ __forceinline__ float load_elem(const float* p, int64_t i) { return p[i]; }
 __device__ __forceinline__ float load_elem(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
 
-template <typename Tin>
+// 32 consecutive row elements as fp32, read as 16-byte vectors (p is 16-byte aligned: rows are,
+// and the offset is a multiple of 32 elements), all issued before any is used.
+constexpr int kVec = 32;
+__device__ __forceinline__ void load_vec(const float* p, float (&v)[kVec]) {
+  float4 q[kVec / 4];
+#pragma unroll
+  for (int i = 0; i < kVec / 4; ++i) q[i] = reinterpret_cast<const float4*>(p)[i];
+#pragma unroll
+  for (int i = 0; i < kVec / 4; ++i) {
+    v[4 * i] = q[i].x;
+    v[4 * i + 1] = q[i].y;
+    v[4 * i + 2] = q[i].z;
+    v[4 * i + 3] = q[i].w;
+  }
+}
+__device__ __forceinline__ void load_vec(const uint16_t* p, float (&v)[kVec]) {
+  uint4 q[kVec / 8];
+#pragma unroll
+  for (int i = 0; i < kVec / 8; ++i) q[i] = reinterpret_cast<const uint4*>(p)[i];
+#pragma unroll
+  for (int i = 0; i < kVec / 8; ++i) {
+    const uint32_t u[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      v[8 * i + 2 * c] = __uint_as_float(u[c] << 16);
+      v[8 * i + 2 * c + 1] = __uint_as_float(u[c] & 0xFFFF0000u);
+    }
+  }
+}
+
+// S: token subsets.  With at most 64 (128) experts, the waves split each group's 8 tokens four
+// (two) ways: thread tid owns expert tid % (256 / S) for tokens tid / (256 / S) + S i, so that no
+// thread multiplies more than 8 / S rows while most of the workgroup would otherwise idle.
+template <typename Tin, int S>
 __global__ __launch_bounds__(kThreads) void router_generic_kernel(const Tin* __restrict__ x, const Tin* __restrict__ w,
                                                                   const float* __restrict__ bias, int64_t T, int d,
                                                                   int n_experts, int K, int normalize,
@@ -40,43 +74,70 @@ __global__ __launch_bounds__(kThreads) void router_generic_kernel(const Tin* __r
   __shared__ float ss[kTok][256];
   __shared__ float qs[kTok][256];
   __shared__ int hist[256];
+  static_assert(kTok * kChunk % kThreads == 0 && kTok % S == 0, "tile shape");
+  constexpr int kSlots = kThreads / S;  // experts per token subset
+  constexpr int kMine = kTok / S;       // tokens per thread
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const bool live = tid < n_experts;
-  const float b = live ? bias[tid] : 0.0f;
+  const int ex = tid % kSlots;  // this thread's expert
+  const int sub = tid / kSlots; // and token subset (wave-uniform)
+  const bool live = ex < n_experts;
+  const float b = live ? bias[ex] : 0.0f;
   hist[tid] = 0;
 
   const int64_t n_groups = (T + kTok - 1) / kTok;
   for (int64_t g = blockIdx.x; g < n_groups; g += gridDim.x) {
     const int64_t t0 = g * kTok;
-    float z[kTok];
+    float z[kMine];  // token sub + S i
 #pragma unroll
-    for (int j = 0; j < kTok; ++j) z[j] = 0.0f;
+    for (int i = 0; i < kMine; ++i) z[i] = 0.0f;
     for (int k0 = 0; k0 < d; k0 += kChunk) {
       const int kn = d - k0 < kChunk ? d - k0 : kChunk;
-      __syncthreads();
-      for (int i = tid; i < kTok * kChunk; i += kThreads) {
+      // All eight loads of this thread are issued before the first is stored (a loop that
+      // stores each element as it arrives waits out one memory latency per element).
+      float xv[kTok * kChunk / kThreads];
+#pragma unroll
+      for (int q = 0; q < kTok * kChunk / kThreads; ++q) {
+        const int i = tid + q * kThreads;
         const int j = i / kChunk, kk = i % kChunk;
-        xs[j][kk] = (t0 + j < T && kk < kn) ? load_elem(x, (t0 + j) * (int64_t)d + k0 + kk) : 0.0f;
+        xv[q] = (t0 + j < T && kk < kn) ? load_elem(x, (t0 + j) * (int64_t)d + k0 + kk) : 0.0f;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < kTok * kChunk / kThreads; ++q) {
+        const int i = tid + q * kThreads;
+        xs[i / kChunk][i % kChunk] = xv[q];
       }
       __syncthreads();
       if (live) {
-        const Tin* wr = w + (int64_t)tid * d + k0;
-        for (int kk = 0; kk < kn; ++kk) {
+        // The thread's weight row, 32 elements per pass read ahead as vectors (one scalar load
+        // per element left every load's latency exposed), multiplied in ascending k as before.
+        const Tin* wr = w + (int64_t)ex * d + k0;
+        int kk = 0;
+        for (; kk + kVec <= kn; kk += kVec) {
+          float wv[kVec];
+          load_vec(wr + kk, wv);
+#pragma unroll
+          for (int u = 0; u < kVec; ++u)
+#pragma unroll
+            for (int i = 0; i < kMine; ++i) z[i] = fmaf(xs[sub + S * i][kk + u], wv[u], z[i]);
+        }
+        for (; kk < kn; ++kk) {
           const float wv = load_elem(wr, kk);
 #pragma unroll
-          for (int j = 0; j < kTok; ++j) z[j] = fmaf(xs[j][kk], wv, z[j]);
+          for (int i = 0; i < kMine; ++i) z[i] = fmaf(xs[sub + S * i][kk], wv, z[i]);
         }
       }
     }
 #pragma unroll
-    for (int j = 0; j < kTok; ++j) {
-      const float s = 1.0f / (1.0f + expf(-z[j]));
-      zs[j][tid] = z[j];
-      ss[j][tid] = s;
-      qs[j][tid] = live ? s + b : -__builtin_inff();
-      if (logits != nullptr && live && t0 + j < T) logits[(t0 + j) * n_experts + tid] = z[j];
+    for (int i = 0; i < kMine; ++i) {
+      const int j = sub + S * i;
+      const float s = 1.0f / (1.0f + expf(-z[i]));
+      zs[j][ex] = z[i];
+      ss[j][ex] = s;
+      qs[j][ex] = live ? s + b : -__builtin_inff();
+      if (logits != nullptr && live && t0 + j < T) logits[(t0 + j) * n_experts + ex] = z[i];
     }
     __syncthreads();
 
@@ -149,7 +210,16 @@ __global__ __launch_bounds__(kThreads) void router_generic_kernel(const Tin* __r
     }
   }
   __syncthreads();
-  if (live && counts != nullptr && hist[tid] != 0) atomicAdd(&counts[tid], hist[tid]);
+  if (tid < n_experts && counts != nullptr && hist[tid] != 0) atomicAdd(&counts[tid], hist[tid]);
+}
+
+template <typename Tin>
+hipError_t launch_s(const RouterArgs& a, int subsets, int grid, int normalize, hipStream_t stream) {
+  auto kernel = subsets == 4 ? router_generic_kernel<Tin, 4>
+                             : subsets == 2 ? router_generic_kernel<Tin, 2> : router_generic_kernel<Tin, 1>;
+  return launch_timed(kernel, dim3(grid), dim3(kThreads), 0, stream, nullptr, a.ev_stop, (const Tin*)a.x,
+                      (const Tin*)a.w, a.bias, a.T, a.d, a.n_experts, a.k, normalize, a.idx, a.gates, a.counts,
+                      a.logits, a.lse);
 }
 
 }  // namespace
@@ -158,13 +228,9 @@ hipError_t launch_router_generic(const RouterArgs& a, hipStream_t stream) {
   const int64_t n_groups = (a.T + kTok - 1) / kTok;
   const int grid = (int)(n_groups < 2048 ? n_groups : 2048);
   const int normalize = (a.flags & ELB_GATES_RAW) ? 0 : 1;
-  if (a.dtype == ELB_F32)
-    return launch_timed(router_generic_kernel<float>, dim3(grid), dim3(kThreads), 0, stream, nullptr, a.ev_stop,
-                        (const float*)a.x, (const float*)a.w, a.bias, a.T, a.d, a.n_experts, a.k, normalize, a.idx,
-                        a.gates, a.counts, a.logits, a.lse);
-  return launch_timed(router_generic_kernel<uint16_t>, dim3(grid), dim3(kThreads), 0, stream, nullptr, a.ev_stop,
-                      (const uint16_t*)a.x, (const uint16_t*)a.w, a.bias, a.T, a.d, a.n_experts, a.k, normalize,
-                      a.idx, a.gates, a.counts, a.logits, a.lse);
+  const int subsets = a.n_experts <= 64 ? 4 : a.n_experts <= 128 ? 2 : 1;
+  if (a.dtype == ELB_F32) return launch_s<float>(a, subsets, grid, normalize, stream);
+  return launch_s<uint16_t>(a, subsets, grid, normalize, stream);
 }
 
 }  // namespace elb

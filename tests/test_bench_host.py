@@ -34,6 +34,9 @@ def test_router_kernel_name_follows_the_tile_switch():
     assert bench.router_kernel_name(65536, 256, 4) == "router_mfma_kernel<4, true, false, 2, 4>"
     assert bench.router_kernel_name(32768, 256, 4) == "router_mfma_kernel<4, true, false, 1, 4>"
     assert bench.router_kernel_name(16384, 200, 2) == "router_mfma_kernel<2, false, false, 1, 2>"
+    assert bench.router_kernel_name(512, 16, 2, "f32") == "router_generic_kernel<float, 4>"
+    assert bench.router_kernel_name(512, 100, 2, "f32") == "router_generic_kernel<float, 2>"
+    assert bench.router_kernel_name(512, 256, 2, "f32") == "router_generic_kernel<float, 1>"
 
 
 def test_dispatch_alg_bytes_large_workload():

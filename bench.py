@@ -405,6 +405,36 @@ def roofline_of(wl, router_ms: float) -> dict:
             "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)}
 
 
+def measured_references(elb, dev, stream, r: dict) -> dict:
+    """What this GPU sustains for the router's two bounds, measured in the same run, beside the
+    published peaks the roofline uses: one streaming read of 4 GiB through the library's
+    elb_stream_xor (best single pass, and 20 passes back to back), and a bf16 GEMM of 8192^3
+    through torch (hipBLASLt), 50 products back to back.  The router's achieved rates are
+    given as fractions of both."""
+    import torch
+
+    n = 4 << 30
+    buf = torch.ones(n // 4, dtype=torch.int32, device=dev)
+    acc = torch.zeros(1, dtype=torch.int32, device=dev)
+    best = time_events(lambda: elb.stream_xor(buf, out=acc), 1, stream)
+    for _ in range(9):
+        best = min(best, time_events(lambda: elb.stream_xor(buf, out=acc), 1, stream))
+    sustained = time_events(lambda: elb.stream_xor(buf, out=acc), 20, stream)
+    del buf
+    a = torch.randn((8192, 8192), device=dev).to(torch.bfloat16)
+    b = torch.randn((8192, 8192), device=dev).to(torch.bfloat16)
+    gemm = time_events(lambda: torch.matmul(a, b), 50, stream)
+    del a, b
+    read_best = n / (best * 1e-3) / 1e9
+    read_sus = n / (sustained * 1e-3) / 1e9
+    gemm_tflops = 2.0 * 8192 ** 3 / (gemm * 1e-3) / 1e12
+    return {"hbm_read_GBps": round(read_sus, 1), "hbm_read_best_GBps": round(read_best, 1),
+            "router_frac_of_read": round(r["achieved"] / read_sus, 4),
+            "gemm_bf16_TFLOPs": round(gemm_tflops, 1), "router_mfma_frac_of_gemm": round(r["mfma_tflops"] / gemm_tflops, 4),
+            "how": "elb_stream_xor over 4 GiB (20 passes back to back; best single pass beside it); "
+                   "torch.matmul bf16 8192^3 (hipBLASLt), 50 back to back"}
+
+
 def bench_config(elb, key: str, dev, stream, steps: int, launches: int) -> dict:
     """Step and router figures of one of the other workloads (one step of the closed-loop one)."""
     import datagen
@@ -586,6 +616,8 @@ def main() -> int:
         line["configs"] = configs
     if loop is not None:
         line["closed_loop"] = loop
+    if wl.dtype == "bf16":
+        line["roofline"]["measured"] = measured_references(elb, dev, stream, r)
     if not args.no_next:
         line["next_rows"] = bench_next_rows(elb, wl, s.xs[0], s.wd, out, stream)
     if args.calibrate_copy:

@@ -342,6 +342,19 @@ def maxvio(counts: torch.Tensor) -> torch.Tensor:
     return out
 
 
+def stream_xor(t: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """One streaming read of t's bytes (16-byte multiple): out[0] ^= the XOR of its 32-bit words
+    (out: one int32 on t's device, zeroed here when not given).  The bench's measured HBM read
+    reference."""
+    _need(t, "t")
+    if out is None:
+        out = torch.zeros(1, dtype=torch.int32, device=t.device)
+    else:
+        _need(out, "out", torch.int32, t.device)
+    check("elb_stream_xor", lib().elb_stream_xor(_ptr(t), t.numel() * t.element_size(), _ptr(out), _stream(t.device)))
+    return out
+
+
 class StepOutputs(NamedTuple):
     """Views of one RouterStep call's outputs (valid until the next call)."""
 

@@ -264,6 +264,13 @@ elb_status elb_maxvio(const int32_t* counts, int32_t n_experts, float* out, elb_
   return from_hip(elb::launch_balance(a, s));
 }
 
+elb_status elb_stream_xor(const void* src, size_t bytes, uint32_t* out, elb_stream_t stream) {
+  if (out == nullptr || (bytes > 0 && src == nullptr)) return ELB_ERR_NULL;
+  if (bytes % 16 != 0) return ELB_ERR_SHAPE;
+  if (!aligned(src, 16) || !aligned(out, 4)) return ELB_ERR_ALIGN;
+  return from_hip(elb::launch_stream_xor(src, (int64_t)(bytes / 16), out, reinterpret_cast<hipStream_t>(stream)));
+}
+
 const char* elb_status_str(elb_status status) {
   switch (status) {
     case ELB_OK: return "ok";

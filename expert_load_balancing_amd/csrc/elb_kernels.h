@@ -69,6 +69,8 @@ hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem,
 }
 
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t value, hipStream_t stream);
+// out[0] ^= XOR of the n16 16-byte words at src (a streaming read; src 16-byte aligned).
+hipError_t launch_stream_xor(const void* src, int64_t n16, uint32_t* out, hipStream_t stream);
 // An empty one-wave kernel whose end time stamp goes into `ev`.
 hipError_t launch_mark(hipEvent_t ev, hipStream_t stream);
 

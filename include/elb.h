@@ -324,6 +324,16 @@ elb_status elb_router_backward(const void* x, int32_t dtype, int64_t T, int32_t 
  */
 elb_status elb_maxvio(const int32_t* counts, int32_t n_experts, float* out, elb_stream_t stream);
 
+/*
+ * A plain streaming read of `bytes` bytes at src: out[0] ^= the XOR of all its 32-bit words
+ * (the caller sets out[0] first).  Not part of the routed step: it is the measured reference
+ * for the router's HBM roofline (the bandwidth one read-only pass over HBM reaches on this
+ * GPU, reported beside the published peak), and the XOR lets a test check every byte was read.
+ * src 16-byte aligned, bytes % 16 == 0 (0 is a no-op), out 4-byte aligned.  Errors: ELB_ERR_NULL,
+ * ELB_ERR_SHAPE (bytes not a multiple of 16), ELB_ERR_ALIGN, ELB_ERR_LAUNCH.
+ */
+elb_status elb_stream_xor(const void* src, size_t bytes, uint32_t* out, elb_stream_t stream);
+
 /* Static description of a status code (never NULL). */
 const char* elb_status_str(elb_status status);
 

@@ -127,6 +127,14 @@ def test_maxvio_rejects(lib):
     assert lib.elb_maxvio(FAKE, 2000, FAKE, None) == SHAPE
 
 
+def test_stream_xor_rejects(lib):
+    assert lib.elb_stream_xor(None, 64, FAKE, None) == NULL
+    assert lib.elb_stream_xor(FAKE, 64, None, None) == NULL
+    assert lib.elb_stream_xor(FAKE, 24, FAKE, None) == SHAPE
+    assert lib.elb_stream_xor(FAKE + 8, 64, FAKE, None) == ALIGN
+    assert lib.elb_stream_xor(FAKE, 64, FAKE + 2, None) == ALIGN
+
+
 def step_args(**kw):
     a = _lib.StepArgs()
     base = dict(x=FAKE, dtype=1, T=4096, d=256, w=FAKE, bias=FAKE, n_experts=256, k=4, flags=2, topk_idx=FAKE,

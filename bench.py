@@ -617,7 +617,10 @@ def main() -> int:
     if loop is not None:
         line["closed_loop"] = loop
     if wl.dtype == "bf16":
-        line["roofline"]["measured"] = measured_references(elb, dev, stream, r)
+        line["roofline"]["measured"] = meas = measured_references(elb, dev, stream, r)
+        for c in (configs or {}).values():
+            if "router_GBps" in c:
+                c["router_frac_of_read"] = round(c["router_GBps"] / meas["hbm_read_GBps"], 4)
     if not args.no_next:
         line["next_rows"] = bench_next_rows(elb, wl, s.xs[0], s.wd, out, stream)
     if args.calibrate_copy:

@@ -12,7 +12,8 @@
 // Layout: a workgroup of 256 threads handles 8 tokens at a time, thread i owning expert i (with
 // at most 64 or 128 experts, the waves split the 8 tokens between them, each thread then owning
 // expert i mod 64 or 128).  The 8 token rows are staged through LDS in chunks of 256 elements;
-// each thread streams its own weight row.  Selection runs one token per wave-pass with a shuffle arg-max.
+// each thread streams its own weight row.  Selection runs one token per wave-pass with a
+// shuffle arg-max.
 #include "device_common.hpp"
 #include "elb_kernels.h"
 
@@ -111,8 +112,8 @@ __global__ __launch_bounds__(kThreads) void router_generic_kernel(const Tin* __r
       }
       __syncthreads();
       if (live) {
-        // The thread's weight row, 32 elements per pass read ahead as vectors (one scalar load
-        // per element left every load's latency exposed), multiplied in ascending k as before.
+        // The thread's weight row, 32 elements per pass read ahead as vectors (a scalar load per
+        // element would expose every load's latency), multiplied in ascending k.
         const Tin* wr = w + (int64_t)ex * d + k0;
         int kk = 0;
         for (; kk + kVec <= kn; kk += kVec) {

@@ -38,7 +38,8 @@
 //     dispatched in index order, so every waited-for block has been dispatched and finishes.  The
 //     wait is also bounded (about a second), so no fault elsewhere can turn it into a hang.
 //     Visibility across the XCDs' separate L2 caches: the scan's results are written and read
-//     with agent-scope atomic stores and loads (coherent accesses that go past the XCD's L2).
+//     with coherent accesses that go past the XCD's L2 (agent-scope atomic loads and stores, and
+//     16-byte stores with the same coherence bit).
 //     A count of finished rows with a release / acquire pair around it would also work, but the
 //     release and acquire write back and invalidate whole L2 caches, once per block, and a
 //     counter that every block polls while the scan blocks add to it holds those adds up: that
@@ -106,6 +107,13 @@ __device__ __forceinline__ void scan_row(int e, int32_t* __restrict__ loads, int
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int32_t* const row = loads + (int64_t)e * stride;
   auto put = [](int32_t* p, int v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+  // A thread's four scanned entries leave in one 16-byte store that carries the same coherence
+  // bit (sc1) an agent-scope atomic store does, so whole lines are written through rather than
+  // four partial ones (-0.8 us per launch at 1024 tiles); each entry carries its own flag, so a
+  // reader sees each of them either stale or final.
+  const __amdgpu_buffer_rsrc_t rrow =
+      __builtin_amdgcn_make_buffer_rsrc(row, (short)0, (int)(stride * 4), 0x00020000);
+  constexpr int kCoherent = 16;  // sc1
   int carry = 0;
   for (int64_t c0 = 0; c0 < n_tiles; c0 += 4 * kThreads) {
     const int64_t t0 = c0 + 4 * tid;  // stride % 4 == 0: t0 < stride covers t0 .. t0 + 3
@@ -126,10 +134,9 @@ __device__ __forceinline__ void scan_row(int e, int32_t* __restrict__ loads, int
     }
     const int excl = carry + before + incl - local;
     if (t0 < stride) {
-      put(row + t0, kScanned | excl);
-      put(row + t0 + 1, kScanned | (excl + v[0]));
-      put(row + t0 + 2, kScanned | (excl + v[0] + v[1]));
-      put(row + t0 + 3, kScanned | (excl + v[0] + v[1] + v[2]));
+      const i32x4 o = {kScanned | excl, kScanned | (excl + v[0]), kScanned | (excl + v[0] + v[1]),
+                       kScanned | (excl + v[0] + v[1] + v[2])};
+      __builtin_amdgcn_raw_buffer_store_b128(o, rrow, (int)(t0 * 4), 0, kCoherent);
     }
     carry += chunk;
     __syncthreads();  // wsum is rewritten by the next chunk

@@ -26,23 +26,77 @@ namespace elb {
 
 constexpr int kBalancePer = 16;  // experts per lane: 64 * 16 = 1024
 
+// Cross-lane steps through the vector ALU's data-parallel primitives (DPP): each is a register
+// move with a lane pattern, a few cycles, where a shuffle (ds_bpermute) is a round trip through
+// the LDS crossbar and waits for it at every step of a reduction.
+namespace dpp {
+constexpr int kXor1 = 0xB1;         // quad_perm [1, 0, 3, 2]: lane i <- i ^ 1
+constexpr int kXor2 = 0x4E;         // quad_perm [2, 3, 0, 1]: lane i <- i ^ 2
+constexpr int kHalfMirror = 0x141;  // lane i <- 7 - i within each 8 lanes
+constexpr int kMirror = 0x140;      // lane i <- 15 - i within each row of 16 lanes
+constexpr int kShr1 = 0x111, kShr2 = 0x112, kShr4 = 0x114, kShr8 = 0x118;  // lane i <- i - n in its row, else 0
+constexpr int kBcast15 = 0x142;     // lane 15 of each row to the whole next row (rows picked by the mask)
+constexpr int kBcast31 = 0x143;     // lane 31 to rows 2 and 3 (picked by the mask)
+
+// The value of the lane CTRL names; 0 in lanes whose source is out of the row, or whose row
+// ROW_MASK leaves out.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int mov(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, true);
+}
+template <int CTRL>
+__device__ __forceinline__ float mov(float v) {
+  return __builtin_bit_cast(float, mov<CTRL>(__builtin_bit_cast(int, v)));
+}
+template <int CTRL, typename T>
+__device__ __forceinline__ T mov64(T v) {  // 8-byte values, as two 4-byte moves
+  const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+  const unsigned long long lo = (unsigned)mov<CTRL>((int)(unsigned)u);
+  const unsigned long long hi = (unsigned)mov<CTRL>((int)(unsigned)(u >> 32));
+  return __builtin_bit_cast(T, lo | (hi << 32));
+}
+template <int CTRL> __device__ __forceinline__ long long mov(long long v) { return mov64<CTRL>(v); }
+template <int CTRL> __device__ __forceinline__ double mov(double v) { return mov64<CTRL>(v); }
+
+__device__ __forceinline__ int lane_value(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+template <typename T>
+__device__ __forceinline__ T lane_value64(T v, int lane) {
+  const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+  const unsigned long long lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)u, lane);
+  const unsigned long long hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(u >> 32), lane);
+  return __builtin_bit_cast(T, lo | (hi << 32));
+}
+__device__ __forceinline__ long long lane_value(long long v, int lane) { return lane_value64(v, lane); }
+__device__ __forceinline__ double lane_value(double v, int lane) { return lane_value64(v, lane); }
+
+// op over the 64 lanes, the same bits in every lane: pairs within each quad, quads within each
+// 8 lanes, those within each row of 16 (every step combines two equal-sized groups, and each
+// lane of a pair applies the commutative op to the same two operands), then the four rows in a
+// fixed order from scalar reads.
+template <typename T, typename Op>
+__device__ __forceinline__ T reduce(T v, Op op) {
+  v = op(v, mov<kXor1>(v));
+  v = op(v, mov<kXor2>(v));
+  v = op(v, mov<kHalfMirror>(v));
+  v = op(v, mov<kMirror>(v));
+  return op(op(lane_value(v, 0), lane_value(v, 16)), op(lane_value(v, 32), lane_value(v, 48)));
+}
+}  // namespace dpp
+
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  return dpp::reduce(v, [](T a, T b) { return a + b; });
 }
 
 __device__ __forceinline__ int wave_max(int v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off));
-  return v;
+  return dpp::reduce(v, [](int a, int b) { return max(a, b); });
 }
 
 __device__ __forceinline__ int wave_min(int v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = min(v, __shfl_xor(v, off));
-  return v;
+  return dpp::reduce(v, [](int a, int b) { return min(a, b); });
 }
 
 // What one lane holds of the update's inputs: its experts lane + 64 r.

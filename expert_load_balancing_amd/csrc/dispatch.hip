@@ -69,13 +69,15 @@ constexpr int kMaxExperts = 256;
 
 using i32x4 = int __attribute__((ext_vector_type(4)));
 
+// Inclusive prefix sum over the wave's 64 lanes with DPP moves (balance_wave.hpp): within each
+// row of 16 by shifts of 1, 2, 4 and 8 lanes, then each row's total into the rows after it.
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int u = __shfl_up(v, off);
-    if (lane >= off) v += u;
-  }
+  v += dpp::mov<dpp::kShr1>(v);
+  v += dpp::mov<dpp::kShr2>(v);
+  v += dpp::mov<dpp::kShr4>(v);
+  v += dpp::mov<dpp::kShr8>(v);
+  v += dpp::mov<dpp::kBcast15, 0xA>(v);  // rows 1 and 3 add the total of rows 0 and 2
+  v += dpp::mov<dpp::kBcast31, 0xC>(v);  // rows 2 and 3 add the total of rows 0-1
   return v;
 }
 

@@ -24,26 +24,48 @@ __global__ __launch_bounds__(64) void balance_layers_kernel(BalanceArgs a) {
 // Router z-loss from per-token log-sum-exps: mean_t lse_t^2 (talk summary "Arcee Halts 400B
 // Blackwell Model Collapse With Dynamic Router Biases", section "Precision Fallbacks, Loss
 // Stabilization, and MaxVio as Data Telemetry": L_z = log^2 sum e^x).  One workgroup; each
-// thread adds its strided share in float64 in index order, then a butterfly per wave and the
-// waves in order: the same bits every run.
+// thread adds its share in float64 in a fixed order, then a reduction per wave and the waves in
+// order: the same bits every run.  The share: the elements before the first 16-byte boundary
+// (at most 3) and after the last one go to thread 0; the 4-element chunks between them go to the
+// threads in turn (chunk c to thread c % 1024), each thread keeping eight 16-byte loads in flight
+// (128 KiB over the workgroup) and adding their elements in index order.
 constexpr int kZThreads = 1024;
+constexpr int kZInFlight = 8;
 __global__ __launch_bounds__(kZThreads) void zloss_kernel(const float* __restrict__ lse, int64_t T,
                                                           float* __restrict__ out) {
   __shared__ double part[kZThreads / 64];
+  typedef __attribute__((ext_vector_type(4))) float f4;
   double acc = 0.0;
-  // Eight loads in flight per thread, then the adds in index order (the same order, and so the
-  // same bits, as one element at a time).
-  int64_t i = threadIdx.x;
-  for (; i + 7 * kZThreads < T; i += 8 * kZThreads) {
-    float v[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] = lse[i + q * kZThreads];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) acc += (double)v[q] * (double)v[q];
+  const int64_t head_room = (int64_t)(((16u - ((uint32_t)(uintptr_t)lse & 15u)) & 15u) / 4u);
+  const int64_t head = head_room < T ? head_room : T;
+  const int64_t n4 = (T - head) / 4;
+  if (threadIdx.x == 0) {
+    for (int64_t i = 0; i < head; ++i) {
+      const double v = lse[i];
+      acc += v * v;
+    }
   }
-  for (; i < T; i += kZThreads) {
-    const double v = lse[i];
-    acc += v * v;
+  const f4* const v4 = reinterpret_cast<const f4*>(lse + head);
+  int64_t c = threadIdx.x;
+  for (; c + (int64_t)(kZInFlight - 1) * kZThreads < n4; c += (int64_t)kZInFlight * kZThreads) {
+    f4 q[kZInFlight];
+#pragma unroll
+    for (int u = 0; u < kZInFlight; ++u) q[u] = v4[c + (int64_t)u * kZThreads];
+#pragma unroll
+    for (int u = 0; u < kZInFlight; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc += (double)q[u][r] * (double)q[u][r];
+  }
+  for (; c < n4; c += kZThreads) {
+    const f4 q = v4[c];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc += (double)q[r] * (double)q[r];
+  }
+  if (threadIdx.x == 0) {
+    for (int64_t i = head + 4 * n4; i < T; ++i) {
+      const double v = lse[i];
+      acc += v * v;
+    }
   }
   acc = wave_sum(acc);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;

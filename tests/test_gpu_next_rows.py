@@ -61,6 +61,24 @@ def test_zloss_matches_oracle(T):
     assert float(again.cpu()[0]) == got  # deterministic
 
 
+@pytest.mark.parametrize("shift", [1, 2, 3])
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 4099, 70001])
+def test_zloss_unaligned_start(T, shift):
+    """lse starting 4, 8 or 12 bytes past a 16-byte boundary (the kernel adds the elements before
+    the first boundary separately): the same bar against the oracle."""
+    rng = np.random.default_rng(T * 7 + shift)
+    lse = (rng.standard_normal(T) * 3 + 5).astype(np.float32)
+    buf = torch.zeros(T + 8, dtype=torch.float32, device="cuda")
+    view = buf[shift:shift + T]
+    view.copy_(torch.from_numpy(lse))
+    assert view.data_ptr() % 16 == 4 * shift
+    out = elb.zloss(view)
+    torch.cuda.synchronize()
+    want = oracle.z_loss_from_lse(lse)
+    got = float(out.cpu()[0])
+    assert abs(got - want) <= 1e-6 * abs(want) + 1e-30, (got, want)
+
+
 def test_zloss_fused_in_step():
     """RouterStep's z-loss equals elb_zloss of its own lse, and its lse matches the oracle's."""
     wl = datagen.WORKLOADS["large"].replace(T=1500, d=512, seed=77, n_clusters=8)

@@ -18,9 +18,10 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("T,d,dispatch,mode", [
-    (4096, 512, True, "smebu"),    # router, then the dispatch launch with the update in it
-    (700, 256, True, "linear"),    # 64-token tiles: the dispatch counts the loads itself
-    (2048, 256, False, "sign"),    # router, then the update launch
+    (40000, 256, True, "smebu"),   # 256-token tiles: router, then the dispatch launch with the update in it
+    (20000, 256, True, "linear"),  # 128-token tiles: the dispatch counts the loads itself
+    (700, 256, True, "smebu"),     # 64-token tiles, ragged tail
+    (2048, 256, False, "sign"),    # 64-token tiles: router, then the update launch
 ])
 def test_replayed_step_matches_eager(T, d, dispatch, mode):
     log(f"graph replay T={T} d={d} dispatch={dispatch} mode={mode}")
